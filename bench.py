@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one batch: build the new tokens'
+cache slots, store their K/V (pa_build_slot_mapping + pa_write_kv), then the
+attention call (pa_decode, or pa_varlen_prefill for packed workloads).  The
+default workload is the LLaMA-2-7B-shaped decode batch (64 sequences, contexts
+U[128,384], 32 q = 32 kv heads, head_dim 128, bf16, 16-token blocks from a
+4096-block pool).
+
+Consecutive timed steps read different layers' caches (same block tables,
+different values, as in a model whose layers share the block manager), so no
+step reads K/V that the previous one left in the 256 MB Infinity Cache.
+
+Prints one JSON line.  `value` is the step's algorithmic HBM bytes over its
+time (GB/s); `roofline` covers the attention kernel, timed with HIP events on
+the stream it is launched on; `cpu_baseline` is the float64 CPU oracle timed on
+a bounded sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode KV-read GB/s (% of HBM peak); prefill TFLOP/s; seq-steps/s"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "decode": ["paged_kv_cache_token_amd/csrc/pa_decode.hip",
+               "paged_kv_cache_token_amd/csrc/pa_internal.h"],
+    "prefill": ["paged_kv_cache_token_amd/csrc/pa_prefill.hip",
+                "paged_kv_cache_token_amd/csrc/pa_internal.h"],
+}
+
+
+def kernel_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES[kind]:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def make_batch(name: str):
+    import workloads as W
+    return {
+        "llama2_decode": W.llama2_decode,
+        "gqa_decode": W.gqa_decode,
+        "shared_prefix_decode": W.shared_prefix_decode,
+        "mixed_step": W.mixed_step,
+        "prefill_chunks": W.prefill_only,
+        "tiny_decode": W.tiny_decode,
+    }[name]()
+
+
+# --------------------------------------------------------------------------
+# algorithmic work (what the step must move / compute at minimum)
+# --------------------------------------------------------------------------
+
+def attention_bytes(b) -> int:
+    """K/V of every attended token (a physical block shared by several
+    sequences counted once), q, out, live block-table entries, lengths."""
+    e = b.elem_bytes
+    tile = b.num_kv_heads * b.block_size * b.head_dim * e
+    ctx = b.context_lens.astype(np.int64)
+    if b.notes.get("prefix_tokens") and not b.notes.get("unshared"):
+        # unique tokens: the shared prompt once plus every private suffix
+        p = b.notes["prefix_tokens"]
+        kv_tokens = p + int((ctx - p).sum())
+    else:
+        kv_tokens = int(ctx.sum())
+    kv = 2 * kv_tokens * b.num_kv_heads * b.head_dim * e
+    qo = 2 * b.total_q * b.num_q_heads * b.head_dim * e
+    live_entries = int(sum(-(-int(c) // b.block_size) for c in ctx))
+    meta = 4 * live_entries + 4 * (2 * b.num_seqs + 1)
+    del tile
+    return kv + qo + meta
+
+
+def write_bytes(b) -> int:
+    """pa_build_slot_mapping + pa_write_kv of the step's new tokens."""
+    row = b.num_kv_heads * b.head_dim * b.elem_bytes
+    slot_map = 4 * (2 * b.num_seqs + 1) + 4 * b.total_q + 8 * b.total_q
+    write = 2 * 2 * b.total_q * row + 8 * b.total_q
+    return slot_map + write
+
+
+def prefill_flops(b) -> int:
+    """Causal (q, k) pairs of the multi-token chunks x 4 * Hq * d (QK^T and PV)."""
+    pairs = 0
+    for c, l in zip(b.context_offsets.astype(np.int64), b.q_lens.astype(np.int64)):
+        if l > 1:
+            pairs += int(l * c + l * (l + 1) // 2)
+    return 4 * b.num_q_heads * b.head_dim * pairs
+
+
+# --------------------------------------------------------------------------
+# CPU baseline: the float64 oracle on a bounded sample
+# --------------------------------------------------------------------------
+
+def cpu_baseline(b, budget_s: float = 10.0) -> dict:
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle
+    from oracle_side import expected, host_state
+
+    hs = host_state(b, device="cuda")
+    n = b.num_seqs
+    order = list(range(n))
+    done_seqs = 0
+    done_bytes = 0
+    per_seq_bytes = _per_seq_attention_bytes(b)
+    t0, c0 = time.perf_counter(), time.process_time()
+    passes = 0
+    while True:
+        for i in order:
+            expected(b, hs, seqs=[i])
+            done_seqs += 1
+            done_bytes += per_seq_bytes[i]
+            if time.perf_counter() - t0 >= budget_s and done_seqs >= min(n, 8):
+                break
+        else:
+            passes += 1
+            continue
+        break
+    wall = time.perf_counter() - t0
+    cpu = time.process_time() - c0
+    del oracle
+    return {
+        "value": round(done_bytes / wall / 1e9, 4),
+        "unit": "GB/s",
+        "cores": max(1, int(round(cpu / wall))),
+        "kind": "oracle",
+        "sample": (f"float64 numpy oracle ({'decode' if b.kind == 'decode' else 'varlen_prefill'})"
+                   f" over {done_seqs} sequences of the workload ({passes} full passes), "
+                   f"{wall:.1f} s wall, {cpu:.1f} s CPU"),
+        "seq_steps_per_s": round(done_seqs / wall, 3),
+    }
+
+
+def _per_seq_attention_bytes(b) -> list[int]:
+    e = b.elem_bytes
+    out = []
+    for i, c in enumerate(b.context_lens.astype(np.int64)):
+        ql = int(b.q_lens[i])
+        out.append(int(2 * c * b.num_kv_heads * b.head_dim * e + 2 * ql * b.num_q_heads * b.head_dim * e))
+    return out
+
+
+# --------------------------------------------------------------------------
+# traffic from committed rocprofv3 counter summaries
+# --------------------------------------------------------------------------
+
+def traffic_from_profiles(workload: str, kind: str):
+    path = os.path.join(PROFILE_DIR, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_hash") != kernel_hash(kind):
+        return None  # the kernel changed since the counters were taken
+    return rec.get("bytes_per_launch")
+
+
+# --------------------------------------------------------------------------
+# main
+# --------------------------------------------------------------------------
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama2_decode",
+                    choices=["llama2_decode", "gqa_decode", "shared_prefix_decode", "mixed_step",
+                             "prefill_chunks", "tiny_decode"])
+    ap.add_argument("--layers", type=int, default=0,
+                    help="layer caches to rotate through (0: enough for >= 1 GiB)")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        return 2
+
+    import torch
+
+    import paged_kv_cache_token_amd as pa  # fails loudly if libpa.so is missing
+    from device_batch import DeviceBatch
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    b = make_batch(args.workload)
+    kind = "decode" if b.kind == "decode" else "prefill"
+    att_bytes = attention_bytes(b)
+    wr_bytes = write_bytes(b)
+    per_layer_ws = att_bytes + wr_bytes
+    layers = args.layers or max(1, min(8, math.ceil((1 << 30) / per_layer_ws)))
+    dbs = [DeviceBatch(b.with_layer(l), device=dev) for l in range(layers)]
+    torch.cuda.synchronize()
+
+    if args.calib_copy_mib:
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    stream = torch.cuda.current_stream(dev)
+    for s in range(args.warmup):
+        dbs[s % layers].step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, synchronized on both sides; HIP events on the
+    # launch stream bracket every attention call
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for s in range(args.steps):
+        d = dbs[s % layers]
+        d.write_new()
+        ev[s][0].record(stream)
+        d.attend()
+        ev[s][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_per_step = ms_total / args.steps
+    att_ms = [a.elapsed_time(z) for a, z in ev]
+    att_avg_ms = float(np.mean(att_ms))
+
+    step_bytes = att_bytes + wr_bytes
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    if kind == "decode" or args.workload == "mixed_step":
+        achieved = att_bytes / (att_avg_ms * 1e-3) / 1e9
+        traffic = traffic_from_profiles(args.workload, "decode")
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": traffic}
+    else:
+        fl = prefill_flops(b)
+        achieved = fl / (att_avg_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFS,
+                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4),
+                    "traffic": traffic_from_profiles(args.workload, "prefill")}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(b, args.cpu_budget)
+
+    ctx = b.context_lens
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if b.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": b.name,
+            "num_seqs": b.num_seqs,
+            "q_heads": b.num_q_heads,
+            "kv_heads": b.num_kv_heads,
+            "head_dim": b.head_dim,
+            "block_size": b.block_size,
+            "pool_blocks": b.num_blocks,
+            "total_q_tokens": b.total_q,
+            "context_min_mean_max": [int(ctx.min()), round(float(ctx.mean()), 1), int(ctx.max())],
+            "layer_caches_rotated": layers,
+            "parallelism": "single-gpu",
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "seq_steps_per_s": round(b.num_seqs / (ms_per_step * 1e-3), 1),
+        "attention_call_us": round(att_avg_ms * 1e3, 2),
+        "attention_bytes": att_bytes,
+        "write_bytes": wr_bytes,
+        "step_bytes": step_bytes,
+        "wall_s_timed": round(wall, 4),
+        "kernel_source_hash": kernel_hash(kind),
+    }
+    if kind == "prefill" or args.workload == "mixed_step":
+        fl = prefill_flops(b)
+        rec["prefill_flops"] = fl
+        rec["prefill_tflops_whole_call"] = round(fl / (att_avg_ms * 1e-3) / 1e12, 2)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

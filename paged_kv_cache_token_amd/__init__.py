@@ -1,0 +1,233 @@
+"""Python binding of libpa, the paged-attention C ABI for MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind ``include/pa.h``.  Tensors are PyTorch device tensors; calls are
+enqueued on the current torch stream of the tensors' device and return without
+waiting.  Importing this package fails loudly when libpa.so has not been built
+(``python -m paged_kv_cache_token_amd.build``); there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "pa.h")
+
+PA_F32, PA_BF16 = 0, 1
+BLOCK_SIZE = 16
+_DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
+
+_c_i32, _c_i64, _c_f32, _c_sz, _c_p = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                                       ctypes.c_size_t, ctypes.c_void_p)
+
+_SIGNATURES = {
+    "pa_version": (_c_i32, []),
+    "pa_status_string": (ctypes.c_char_p, [_c_i32]),
+    "pa_build_slot_mapping": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_i32, _c_i64, _c_i32, _c_i32, _c_p]),
+    "pa_write_kv": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i32, _c_i32, _c_i32, _c_i64,
+                             _c_i32, _c_p]),
+    "pa_decode_workspace_size": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "pa_decode": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32,
+                           _c_i32, _c_i32, _c_i32, _c_i64, _c_f32, _c_i32, _c_p, _c_sz, _c_p]),
+    "pa_varlen_workspace_size": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "pa_varlen_prefill": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32,
+                                   _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                   _c_i64, _c_f32, _c_i32, _c_p, _c_sz, _c_p]),
+}
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built: run `python -m paged_kv_cache_token_amd.build` "
+            "(hipcc --offload-arch=gfx950). The library has no non-HIP fallback.")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class PAError(RuntimeError):
+    def __init__(self, call: str, status: int):
+        self.status = status
+        super().__init__(f"{call}: status {status} ({status_string(status)})")
+
+
+def version() -> int:
+    return int(lib.pa_version())
+
+
+def status_string(status: int) -> str:
+    return lib.pa_status_string(status).decode()
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/pa.h declares."""
+    text = open(HEADER_PATH).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\*]+\s+)+\**(pa_\w+)\s*\(", text, re.M)))
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers
+# --------------------------------------------------------------------------
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+
+
+def _check(call: str, status: int):
+    if status != 0:
+        raise PAError(call, status)
+
+
+def _cache_dims(k_cache: torch.Tensor):
+    num_blocks, num_kv_heads, block_size, head_dim = k_cache.shape
+    return num_blocks, num_kv_heads, block_size, head_dim
+
+
+def _workspace(size: int, like: torch.Tensor, workspace):
+    if size == 0:
+        return workspace, 0 if workspace is None else workspace.numel()
+    if workspace is None:
+        workspace = torch.empty(size, dtype=torch.uint8, device=like.device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+# --------------------------------------------------------------------------
+# calls
+# --------------------------------------------------------------------------
+
+def build_slot_mapping(cu_seqlens: torch.Tensor, context_offsets: torch.Tensor,
+                       block_tables: torch.Tensor, num_tokens: int,
+                       out: torch.Tensor | None = None) -> torch.Tensor:
+    """int64 [num_tokens] cache slot of every new token (pa_build_slot_mapping)."""
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _need(context_offsets, "context_offsets", torch.int32, 1)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    if out is None:
+        out = torch.empty(num_tokens, dtype=torch.int64, device=cu_seqlens.device)
+    _need(out, "out", torch.int64, 1)
+    n = context_offsets.shape[0]
+    _check("pa_build_slot_mapping", lib.pa_build_slot_mapping(
+        _ptr(out), _ptr(cu_seqlens), _ptr(context_offsets), _ptr(block_tables), n, num_tokens,
+        block_tables.shape[1], BLOCK_SIZE, _stream(cu_seqlens)))
+    return out
+
+
+def write_kv(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor,
+             v_cache: torch.Tensor, slot_mapping: torch.Tensor) -> None:
+    """Store key/value [T, Hkv, d] into their cache slots (pa_write_kv)."""
+    for t, nm in ((key, "key"), (value, "value"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, nm)
+    _need(slot_mapping, "slot_mapping", torch.int64, 1)
+    num_blocks, hkv, bs, d = _cache_dims(k_cache)
+    if key.dtype not in _DTYPES or len({key.dtype, value.dtype, k_cache.dtype, v_cache.dtype}) != 1:
+        raise TypeError("key, value and caches must share dtype float32 or bfloat16")
+    if key.shape != value.shape or key.dim() != 3 or key.shape[1:] != (hkv, d):
+        raise ValueError("key/value must be [num_tokens, num_kv_heads, head_dim]")
+    if v_cache.shape != k_cache.shape or slot_mapping.shape[0] != key.shape[0]:
+        raise ValueError("cache shapes or slot_mapping length mismatch")
+    _check("pa_write_kv", lib.pa_write_kv(
+        _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), key.shape[0],
+        hkv, d, bs, num_blocks, _DTYPES[key.dtype], _stream(key)))
+
+
+def decode_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int, max_context_len: int,
+                          dtype: torch.dtype) -> int:
+    return int(lib.pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
+                                            _DTYPES[dtype]))
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+           block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+           scale: float | None = None, out: torch.Tensor | None = None,
+           workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Paged decode attention (pa_decode); returns out [num_seqs, Hq, d]."""
+    for t, nm in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, nm)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    num_blocks, hkv, bs, d = _cache_dims(k_cache)
+    n, hq, dq = q.shape
+    if dq != d or q.dtype not in _DTYPES or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q / cache head_dim or dtype mismatch")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype)
+    scale = float(d ** -0.5 if scale is None else scale)
+    size = decode_workspace_size(n, hq, d, max_context_len, q.dtype)
+    workspace, ws_bytes = _workspace(size, q, workspace)
+    _check("pa_decode", lib.pa_decode(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        n, hq, hkv, d, bs, block_tables.shape[1], int(max_context_len), num_blocks, scale,
+        _DTYPES[q.dtype], _ptr(workspace), ws_bytes, _stream(q)))
+    return out
+
+
+def varlen_workspace_size(num_seqs: int, total_q_tokens: int, num_q_heads: int,
+                          num_kv_heads: int, head_dim: int, max_context_len: int,
+                          dtype: torch.dtype) -> int:
+    return int(lib.pa_varlen_workspace_size(num_seqs, total_q_tokens, num_q_heads, num_kv_heads,
+                                            head_dim, max_context_len, _DTYPES[dtype]))
+
+
+def varlen_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   cu_seqlens: torch.Tensor, context_offsets: torch.Tensor,
+                   block_tables: torch.Tensor, max_q_len: int, max_context_len: int,
+                   scale: float | None = None, out: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Packed super-sequence attention (pa_varlen_prefill); out [total_q, Hq, d]."""
+    for t, nm in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, nm)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    _need(context_offsets, "context_offsets", torch.int32, 1)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    num_blocks, hkv, bs, d = _cache_dims(k_cache)
+    total_q, hq, dq = q.shape
+    if dq != d or q.dtype not in _DTYPES or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q / cache head_dim or dtype mismatch")
+    n = context_offsets.shape[0]
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype)
+    scale = float(d ** -0.5 if scale is None else scale)
+    size = varlen_workspace_size(n, total_q, hq, hkv, d, max_context_len, q.dtype)
+    workspace, ws_bytes = _workspace(size, q, workspace)
+    _check("pa_varlen_prefill", lib.pa_varlen_prefill(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens), _ptr(context_offsets),
+        _ptr(block_tables), n, total_q, int(max_q_len), int(max_context_len), hq, hkv, d, bs,
+        block_tables.shape[1], num_blocks, scale, _DTYPES[q.dtype], _ptr(workspace), ws_bytes,
+        _stream(q)))
+    return out
+
+
+__all__ = ["PAError", "PA_F32", "PA_BF16", "BLOCK_SIZE", "build_slot_mapping", "decode",
+           "decode_workspace_size", "header_functions", "lib", "status_string",
+           "varlen_prefill", "varlen_workspace_size", "version", "write_kv"]

@@ -1,0 +1,212 @@
+// pa_api.hip -- the C ABI: host-side argument checks, workspace sizing and
+// dispatch to the kernels.  Nothing here touches the GPU before every check
+// has passed, so a call that returns an error has enqueued nothing.
+
+#include "../../include/pa.h"
+#include "pa_internal.h"
+
+using namespace pa;
+
+namespace {
+
+bool dtype_ok(int32_t dt) { return dt == PA_F32 || dt == PA_BF16; }
+int elem_bytes(int32_t dt) { return dt == PA_BF16 ? 2 : 4; }
+bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
+bool heads_ok(int32_t hq, int32_t hkv) {
+  if (hq <= 0 || hkv <= 0 || hq % hkv != 0) return false;
+  const int g = hq / hkv;
+  return g == 1 || g == 2 || g == 4 || g == 8;
+}
+int32_t from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// varlen workspace = [decode partials][prefill work list]
+size_t varlen_decode_part_bytes(int32_t num_seqs, int32_t hq, int32_t d, int32_t max_ctx) {
+  return align_up(decode_ws_floats(num_seqs, hq, d, decode_max_parts(max_ctx)) * sizeof(float));
+}
+size_t varlen_work_bytes(int32_t num_seqs, int32_t total_q, int32_t group) {
+  // one count + two ints per item
+  return align_up((size_t)(1 + 2 * prefill_work_capacity(num_seqs, total_q, group)) * sizeof(int32_t));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pa_version(void) { return PA_VERSION; }
+
+const char* pa_status_string(int32_t status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case PA_ERR_UNSUPPORTED:
+      return "unsupported dtype, head_dim, block_size or query/kv head ratio";
+    case PA_ERR_INVALID_ARGUMENT: return "negative or inconsistent size argument";
+    case PA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than the size query returned";
+    case PA_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+    default: return "unknown status";
+  }
+}
+
+int32_t pa_build_slot_mapping(int64_t* slot_mapping, const int32_t* cu_seqlens,
+                              const int32_t* context_offsets, const int32_t* block_tables,
+                              int32_t num_seqs, int64_t num_tokens, int32_t max_blocks_per_seq,
+                              int32_t block_size, void* stream) {
+  if (num_seqs < 0 || num_tokens < 0 || max_blocks_per_seq < 0) return PA_ERR_INVALID_ARGUMENT;
+  if (block_size != PA_BLOCK_SIZE) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || num_tokens == 0) return PA_OK;
+  if (!slot_mapping || !cu_seqlens || !context_offsets || !block_tables) return PA_ERR_NULL_POINTER;
+  if (max_blocks_per_seq == 0) return PA_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_slot_mapping(slot_mapping, cu_seqlens, context_offsets, block_tables,
+                                      num_seqs, max_blocks_per_seq,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int32_t pa_write_kv(const void* key, const void* value, void* k_cache, void* v_cache,
+                    const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t dtype,
+                    void* stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(head_dim) || block_size != PA_BLOCK_SIZE)
+    return PA_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_INVALID_ARGUMENT;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL_POINTER;
+  return from_hip(launch_write_kv(key, value, k_cache, v_cache, slot_mapping, num_tokens,
+                                  num_kv_heads, head_dim, num_blocks, elem_bytes(dtype),
+                                  static_cast<hipStream_t>(stream)));
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                int32_t max_context_len, int32_t dtype) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || !head_dim_ok(head_dim) || !dtype_ok(dtype)) return 0;
+  return decode_ws_floats(num_seqs, num_q_heads, head_dim, decode_max_parts(max_context_len)) *
+         sizeof(float);
+}
+
+int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                  int32_t block_size, int32_t max_blocks_per_seq, int32_t max_context_len,
+                  int64_t num_blocks, float scale, int32_t dtype, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(head_dim) || block_size != PA_BLOCK_SIZE ||
+      !heads_ok(num_q_heads, num_kv_heads))
+    return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || num_blocks <= 0)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return PA_ERR_NULL_POINTER;
+  const size_t need =
+      pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, dtype);
+  if (workspace_bytes < need) return PA_ERR_WORKSPACE_TOO_SMALL;
+  if (need > 0 && !workspace) return PA_ERR_NULL_POINTER;
+
+  DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.num_blocks = num_blocks;
+  a.scale = scale;
+  a.dtype = dtype;
+  a.varlen = false;
+  a.ws = static_cast<float*>(workspace);
+  a.max_parts = decode_max_parts(max_context_len);
+  return from_hip(launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t pa_varlen_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len,
+                                int32_t dtype) {
+  if (num_seqs <= 0 || total_q_tokens < 0 || !head_dim_ok(head_dim) || dtype != PA_BF16 ||
+      !heads_ok(num_q_heads, num_kv_heads))
+    return 0;
+  return varlen_decode_part_bytes(num_seqs, num_q_heads, head_dim, max_context_len) +
+         varlen_work_bytes(num_seqs, total_q_tokens, num_q_heads / num_kv_heads);
+}
+
+int32_t pa_varlen_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* cu_seqlens, const int32_t* context_offsets,
+                          const int32_t* block_tables, int32_t num_seqs, int32_t total_q_tokens,
+                          int32_t max_q_len, int32_t max_context_len, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                          int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                          int32_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != PA_BF16 || !head_dim_ok(head_dim) || block_size != PA_BLOCK_SIZE ||
+      !heads_ok(num_q_heads, num_kv_heads))
+    return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || total_q_tokens < 0 || max_q_len < 0 || max_context_len < 0 ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (num_seqs == 0 || total_q_tokens == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !cu_seqlens || !context_offsets || !block_tables)
+    return PA_ERR_NULL_POINTER;
+  const size_t need = pa_varlen_workspace_size(num_seqs, total_q_tokens, num_q_heads,
+                                               num_kv_heads, head_dim, max_context_len, dtype);
+  if (workspace_bytes < need) return PA_ERR_WORKSPACE_TOO_SMALL;
+  if (!workspace) return PA_ERR_NULL_POINTER;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const size_t dec_bytes =
+      varlen_decode_part_bytes(num_seqs, num_q_heads, head_dim, max_context_len);
+
+  // single-token rows: the decode kernels in varlen mode
+  DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.cu_seqlens = cu_seqlens;
+  a.context_offsets = context_offsets;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.num_blocks = num_blocks;
+  a.scale = scale;
+  a.dtype = dtype;
+  a.varlen = true;
+  a.ws = reinterpret_cast<float*>(ws);
+  a.max_parts = decode_max_parts(max_context_len);
+  hipError_t err = launch_decode(a, s);
+  if (err != hipSuccess) return PA_ERR_HIP;
+  if (max_q_len <= 1) return PA_OK;
+
+  // multi-token chunks: the matrix-core prefill kernel
+  PrefillArgs p{};
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.cu_seqlens = cu_seqlens;
+  p.context_offsets = context_offsets;
+  p.block_tables = block_tables;
+  p.num_seqs = num_seqs;
+  p.total_q_tokens = total_q_tokens;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.max_context_len = max_context_len;
+  p.num_blocks = num_blocks;
+  p.scale = scale;
+  p.work = reinterpret_cast<int32_t*>(ws + dec_bytes);
+  p.work_cap = prefill_work_capacity(num_seqs, total_q_tokens, num_q_heads / num_kv_heads);
+  return from_hip(launch_prefill(p, s));
+}
+
+}  // extern "C"

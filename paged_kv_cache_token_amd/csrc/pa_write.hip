@@ -1,0 +1,86 @@
+// pa_write.hip -- slot mapping and the KV-slot scatter.
+//
+// "vLLM изнутри: как устроен движок для быстрого инференса LLM", forward-pass
+// paragraph: the model runner builds a slot mapping for the step's new tokens.
+// "vLLM：颠覆大模型推理的高效API服务引擎深度解析", §1.3: each new token's K/V
+// vectors are stored into its allocated physical block.
+//
+// Both kernels are pure data movement.  The scatter moves every (token, kv head)
+// row as 16-byte vectors: consecutive lanes take consecutive 16-byte pieces of
+// the same source row, so both the read of key/value and the write into the
+// 16 * head_dim tile of the destination block are fully coalesced.
+
+#include <algorithm>
+
+#include "pa_internal.h"
+
+namespace pa {
+
+// One workgroup per sequence; lanes walk that sequence's new tokens.
+__global__ __launch_bounds__(256) void slot_mapping_kernel(
+    int64_t* __restrict__ slot_mapping, const int32_t* __restrict__ cu_seqlens,
+    const int32_t* __restrict__ context_offsets, const int32_t* __restrict__ block_tables,
+    int32_t max_blocks_per_seq) {
+  const int seq = blockIdx.x;
+  const int lo = cu_seqlens[seq];
+  const int hi = cu_seqlens[seq + 1];
+  const int base = context_offsets[seq];
+  const int32_t* table = block_tables + (int64_t)seq * max_blocks_per_seq;
+  for (int t = lo + (int)threadIdx.x; t < hi; t += blockDim.x) {
+    const int pos = base + (t - lo);
+    const int logical = pos / kBlockSize;
+    int64_t slot = -1;
+    if (pos >= 0 && logical < max_blocks_per_seq)
+      slot = (int64_t)table[logical] * kBlockSize + (pos % kBlockSize);
+    slot_mapping[t] = slot;
+  }
+}
+
+// One thread per 16-byte piece of a (token, kv head) row (grid-stride).
+__global__ __launch_bounds__(256) void write_kv_kernel(
+    const uint4* __restrict__ key, const uint4* __restrict__ value, uint4* __restrict__ k_cache,
+    uint4* __restrict__ v_cache, const int64_t* __restrict__ slot_mapping, int64_t total_pieces,
+    int32_t num_kv_heads, int32_t pieces_per_row, int64_t num_slots) {
+  const int64_t per_token = (int64_t)num_kv_heads * pieces_per_row;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total_pieces;
+       idx += stride) {
+    const int64_t token = idx / per_token;
+    const int rem = (int)(idx - token * per_token);
+    const int head = rem / pieces_per_row;
+    const int piece = rem - head * pieces_per_row;
+    const int64_t slot = slot_mapping[token];
+    if (slot < 0 || slot >= num_slots) continue;
+    const int64_t blk = slot / kBlockSize;
+    const int off = (int)(slot - blk * kBlockSize);
+    const int64_t dst = ((blk * num_kv_heads + head) * kBlockSize + off) * pieces_per_row + piece;
+    k_cache[dst] = key[idx];
+    v_cache[dst] = value[idx];
+  }
+}
+
+hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* cu_seqlens,
+                               const int32_t* context_offsets, const int32_t* block_tables,
+                               int32_t num_seqs, int32_t max_blocks_per_seq, hipStream_t stream) {
+  if (num_seqs == 0) return hipSuccess;
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3(num_seqs), dim3(256), 0, stream, slot_mapping,
+                     cu_seqlens, context_offsets, block_tables, max_blocks_per_seq);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_kv(const void* key, const void* value, void* k_cache, void* v_cache,
+                           const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                           int32_t head_dim, int64_t num_blocks, int32_t elem_bytes,
+                           hipStream_t stream) {
+  const int pieces_per_row = head_dim * elem_bytes / 16;
+  const int64_t total = num_tokens * num_kv_heads * pieces_per_row;
+  if (total == 0) return hipSuccess;
+  const int64_t grid = std::min<int64_t>((total + 255) / 256, 1 << 20);
+  hipLaunchKernelGGL(write_kv_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                     static_cast<const uint4*>(key), static_cast<const uint4*>(value),
+                     static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), slot_mapping,
+                     total, num_kv_heads, pieces_per_row, num_blocks * kBlockSize);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,170 @@
+"""GPU parity of slot mapping, KV write and paged decode against the oracle.
+
+Bars: slot mapping and cache contents bit-exact (NaN canaries in every slot
+nobody wrote must survive); attention max-abs error <= 1e-5 for fp32 and
+<= 2e-2 for bf16 (fp32 accumulation) against the float64 oracle; placement,
+sharing and repeat runs bit-identical on the GPU.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from conftest import host_bits
+from oracle_side import bits_equal, expected, host_state
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def _device_batch(batch):
+    from device_batch import DeviceBatch
+    return DeviceBatch(batch)
+
+
+def _max_err(got: torch.Tensor, want: np.ndarray) -> float:
+    g = got.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(g).all()
+    return float(np.abs(g - want).max()) if want.size else 0.0
+
+
+def _check_decode(batch, seqs=None, check_pools=True):
+    say(batch.name, "n", batch.num_seqs, "maxctx", batch.max_context_len, batch.dtype,
+        "d", batch.head_dim, "g", batch.num_q_heads // batch.num_kv_heads)
+    db = _device_batch(batch)
+    out = db.step()
+    torch.cuda.synchronize()
+    hs = host_state(batch)
+    assert np.array_equal(db.slots.cpu().numpy(), hs.new_slots), "slot mapping differs"
+    if check_pools:
+        assert bits_equal(host_bits(db.k_cache), hs.k_cache), "k_cache differs"
+        assert bits_equal(host_bits(db.v_cache), hs.v_cache), "v_cache differs"
+    want = expected(batch, hs, seqs)
+    got = out if seqs is None else out[torch.as_tensor(list(seqs), device=out.device)]
+    err = _max_err(got, want)
+    say("max abs err", err)
+    assert err <= TOL[batch.dtype], err
+    return db, out
+
+
+def test_tiny_decode_fp32(gpu):
+    _check_decode(W.tiny_decode())
+
+
+@pytest.mark.parametrize("dtype,d,hq,hkv", [
+    ("f32", 64, 4, 4), ("f32", 128, 8, 2), ("bf16", 128, 8, 8), ("bf16", 128, 16, 4),
+    ("bf16", 64, 8, 4), ("bf16", 128, 16, 2), ("bf16", 128, 32, 4), ("f32", 64, 16, 2),
+])
+def test_decode_ragged_multi_partition(gpu, dtype, d, hq, hkv):
+    # exact fill, one over, partial blocks, partition edges (512) and several partitions
+    lens = [1, 2, 15, 16, 17, 100, 511, 512, 513, 1024, 1100, 2049]
+    batch = W.decode_batch(f"ragged_{dtype}_{d}_{hq}_{hkv}", 7, lens, hq, hkv, d, dtype,
+                           pool_factor=1.3)
+    _check_decode(batch)
+
+
+def test_decode_zero_context(gpu):
+    """A sequence with context 0 gets a zero row; the others are unaffected."""
+    batch = W.decode_batch("zero_ctx", 8, [1, 5, 1, 600], 8, 2, 128, "bf16", pool_factor=1.5)
+    db = _device_batch(batch)
+    base = db.step().clone()
+    db.context_lens[0] = 0
+    db.context_lens[2] = 0
+    db.out.fill_(7.0)
+    out = db.attend()
+    torch.cuda.synchronize()
+    assert (out[0] == 0).all() and (out[2] == 0).all()
+    assert torch.equal(out[1], base[1]) and torch.equal(out[3], base[3])
+
+
+def test_decode_garbage_tail_entries_and_bad_ids(gpu):
+    """Table entries past ceil(ctx/16) are never read: poisoning them (even with
+    out-of-range ids) changes nothing."""
+    batch = W.decode_batch("tail", 9, [5, 16, 33, 700], 8, 2, 128, "bf16", pool_factor=1.5)
+    db = _device_batch(batch)
+    base = db.step().clone()
+    bt = db.block_tables.clone()
+    for i, n in enumerate(batch.context_lens):
+        live = -(-int(n) // 16)
+        bt[i, live:] = -7 if i % 2 else 10 ** 6
+    db.block_tables.copy_(bt)
+    again = db.attend().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(base, again)
+
+
+def test_decode_placement_invariance(gpu):
+    lens = [3, 40, 333, 900, 1500]
+    a = W.decode_batch("place_a", 10, lens, 16, 4, 128, "bf16", pool_factor=2.0, perm_rng_seed=1)
+    b = W.decode_batch("place_b", 10, lens, 16, 4, 128, "bf16", pool_factor=2.0, perm_rng_seed=2)
+    assert not np.array_equal(a.block_tables, b.block_tables)
+    oa = _device_batch(a).step().clone()
+    ob = _device_batch(b).step().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob)
+
+
+def test_decode_deterministic(gpu):
+    batch = W.decode_batch("repeat", 11, [700, 1300, 64, 2000], 32, 8, 128, "bf16")
+    db = _device_batch(batch)
+    o1 = db.step().clone()
+    o2 = db.attend().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_shared_prefix_small_equals_unshared(gpu):
+    kw = dict(n=6, suffix_range=(16, 1500))
+    shared = W.shared_prefix_decode(**kw)
+    unshared = W.shared_prefix_decode(unshared=True, **kw)
+    db_s, out_s = _check_decode(shared)
+    out_u = _device_batch(unshared).step()
+    torch.cuda.synchronize()
+    assert torch.equal(out_s, out_u)
+
+
+def test_varlen_decode_rows_equal_decode(gpu):
+    """All-single-token rows through the packed call take the decode kernels:
+    identical output to pa_decode."""
+    import paged_kv_cache_token_amd as pa
+    lens = [1, 17, 600, 1200, 64]
+    batch = W.decode_batch("rows", 12, lens, 32, 8, 128, "bf16", pool_factor=1.2)
+    db = _device_batch(batch)
+    dec = db.step().clone()
+    vl = pa.varlen_prefill(db.q, db.k_cache, db.v_cache, db.cu_seqlens, db.context_offsets,
+                           db.block_tables, 1, batch.max_context_len, batch.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(dec, vl)
+
+
+# ---- the full-size configurations --------------------------------------------
+
+def test_llama2_decode_full(gpu):
+    _check_decode(W.llama2_decode())
+
+
+def test_gqa_decode_full_sampled(gpu):
+    batch = W.gqa_decode()
+    order = np.argsort(batch.context_lens)
+    seqs = sorted(set(order[:4].tolist() + order[-6:].tolist() + list(range(0, 256, 23))))
+    _check_decode(batch, seqs=seqs, check_pools=False)
+
+
+def test_shared_prefix_full_sampled_and_unshared(gpu):
+    shared = W.shared_prefix_decode()
+    order = np.argsort(shared.context_lens)
+    seqs = sorted(set([0, 1, 64, 127] + order[:2].tolist() + order[-2:].tolist()))
+    _, out_s = _check_decode(shared, seqs=seqs, check_pools=False)
+    out_s = out_s.clone()
+    torch.cuda.empty_cache()
+    out_u = _device_batch(W.shared_prefix_decode(unshared=True)).step()
+    torch.cuda.synchronize()
+    assert torch.equal(out_s, out_u)

@@ -259,6 +259,7 @@ def decode_batch(name: str, seed: int, ctx_lens, num_q_heads: int, num_kv_heads:
     """A decode step: each sequence appends one token and attends to ctx_len keys."""
     rng = np.random.default_rng(seed if perm_rng_seed is None else perm_rng_seed)
     ctx = np.asarray(ctx_lens, dtype=np.int32)
+    assert (ctx >= 1).all(), "a decode row attends at least its own new token"
     need = [_alloc_count(c, BLOCK_SIZE) for c in ctx]
     if pool is None:
         pool = max(1, int(np.ceil(sum(need) * pool_factor)))
@@ -267,9 +268,7 @@ def decode_batch(name: str, seed: int, ctx_lens, num_q_heads: int, num_kv_heads:
     bt = _place(rng, need, pool, maxb)
     n = len(ctx)
     cu = np.arange(n + 1, dtype=np.int32)
-    c_off = np.maximum(ctx - 1, 0).astype(np.int32)
-    # a zero-length context has no new token either: its q row still exists
-    # (decode shape), and the call must return a zero row for it.
+    c_off = (ctx - 1).astype(np.int32)
     fseq, fstart, fcu = _segments_plain(c_off)
     return PagedBatch(name=name, dtype=dtype, num_q_heads=num_q_heads,
                       num_kv_heads=num_kv_heads, head_dim=head_dim, num_blocks=pool,

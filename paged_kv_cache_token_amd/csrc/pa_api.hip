@@ -24,7 +24,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // varlen workspace = [decode partials][prefill work list]
 size_t varlen_decode_part_bytes(int32_t num_seqs, int32_t hq, int32_t d, int32_t max_ctx) {
-  return align_up(decode_ws_floats(num_seqs, hq, d, decode_max_parts(max_ctx)) * sizeof(float));
+  return align_up(decode_ws_bytes(num_seqs, hq, d, decode_max_parts(max_ctx)));
 }
 size_t varlen_work_bytes(int32_t num_seqs, int32_t total_q, int32_t group) {
   // one count + two ints per item
@@ -81,8 +81,7 @@ int32_t pa_write_kv(const void* key, const void* value, void* k_cache, void* v_c
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                 int32_t max_context_len, int32_t dtype) {
   if (num_seqs <= 0 || num_q_heads <= 0 || !head_dim_ok(head_dim) || !dtype_ok(dtype)) return 0;
-  return decode_ws_floats(num_seqs, num_q_heads, head_dim, decode_max_parts(max_context_len)) *
-         sizeof(float);
+  return decode_ws_bytes(num_seqs, num_q_heads, head_dim, decode_max_parts(max_context_len));
 }
 
 int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -121,8 +120,10 @@ int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_c
   a.scale = scale;
   a.dtype = dtype;
   a.varlen = false;
-  a.ws = static_cast<float*>(workspace);
-  a.max_parts = decode_max_parts(max_context_len);
+  decode_config(num_seqs, num_kv_heads, max_context_len, &a.waves, &a.part_tokens, &a.buffers);
+  a.max_parts = decode_max_parts(max_context_len, a.part_tokens);
+  if (a.max_parts > 1)
+    a.ws = decode_ws_layout(workspace, num_seqs, num_q_heads, head_dim, a.max_parts);
   return from_hip(launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -180,8 +181,9 @@ int32_t pa_varlen_prefill(void* out, const void* q, const void* k_cache, const v
   a.scale = scale;
   a.dtype = dtype;
   a.varlen = true;
-  a.ws = reinterpret_cast<float*>(ws);
-  a.max_parts = decode_max_parts(max_context_len);
+  decode_config(num_seqs, num_kv_heads, max_context_len, &a.waves, &a.part_tokens, &a.buffers);
+  a.max_parts = decode_max_parts(max_context_len, a.part_tokens);
+  if (a.max_parts > 1) a.ws = decode_ws_layout(ws, num_seqs, num_q_heads, head_dim, a.max_parts);
   hipError_t err = launch_decode(a, s);
   if (err != hipSuccess) return PA_ERR_HIP;
   if (max_q_len <= 1) return PA_OK;

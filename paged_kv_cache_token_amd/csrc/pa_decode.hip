@@ -1,24 +1,26 @@
 // pa_decode.hip -- paged decode attention: split-K over fixed partitions of the
-// context, online softmax, and a cross-partition combine.
+// context, online softmax, and a cross-partition merge.
 //
 // "vLLM：颠覆大模型推理的高效API服务引擎深度解析", §1.3 (attention reads the
 // blocks scattered over the pool through the block table) and §2.2 (one fused
 // kernel reads the KV cache straight from the physical blocks);
 // "vLLM изнутри: как устроен движок для быстрого инференса LLM", the paragraph on
 // the stages of a step (decode reads every cached K/V for one query token and
-// is bound by memory bandwidth).  The split of the softmax over partitions with
-// a later rescaled merge is the chunked-attention idea named in
-// "vLLMつかったら、ベクトル検索サーバーが高速化して安定性も向上した" (the
-// flash-attention paragraph: attention computed in small pieces in on-chip
-// memory).
+// is bound by memory bandwidth).  Splitting the softmax over pieces of the
+// context and merging them with a rescale is the chunked-attention idea of the
+// flash-attention paragraph in "vLLMつかったら、ベクトル検索サーバーが高速化して
+// 安定性も向上した".
 //
 // Work decomposition (gfx950, wave64):
-//   * one workgroup = one (sequence, kv head, partition of kPartitionTokens
-//     tokens); it serves all g query heads that share the kv head, so every K/V
-//     tile is read from HBM once per step;
-//   * 4 waves per workgroup take the partition's 16-token blocks round-robin;
-//     each wave keeps the next block's K and V in registers while it computes
-//     the current one;
+//   * a work item is one (sequence, partition of the context) for one kv head;
+//     a workgroup of 1, 2 or 4 waves serves all g query heads of that kv head,
+//     so each K/V tile is read from HBM once per step;
+//   * the waves take the partition's 16-token blocks round-robin.  A wave
+//     reads its block-table entries once (one entry per lane, issued together
+//     with the context length and the query) and broadcasts them with
+//     readlane, so the only vector loads in its loop are K and V; it keeps the
+//     next block's K and V in flight while it computes the current one (two
+//     register buffers, alternating);
 //   * a (block, kv head) tile is 16 * head_dim contiguous elements, so one
 //     wave-wide 16-byte-per-lane load reads 1 KB of consecutive memory; lane l
 //     holds the 16-byte piece (l % LPT) of token row (l / LPT) + k * (64 / LPT);
@@ -26,16 +28,25 @@
 //     inside the LPT-lane group that holds one token row (LPT = 16 for bf16 at
 //     head_dim 128: exactly one DPP row);
 //   * each lane group keeps its own running (max, sum, accumulator) over the
-//     token rows it holds; groups are merged once at the end, first across the
+//     token rows it holds; groups are merged at the end of the item, across the
 //     wave with lane exchanges, then across the 4 waves in LDS;
-//   * a partition's result goes straight to `out` when the sequence has a
-//     single partition; otherwise (max, sum, accumulator) go to the workspace
-//     and a second kernel merges the partitions in fixed order.
+//   * an item whose sequence has one partition writes `out` directly.  Otherwise
+//     it stores (max, sum, accumulator) in the workspace, and a merge kernel
+//     combines the sequence's partitions in ascending order and writes `out`
+//     (a separate launch: the kernel boundary publishes the partials to every
+//     XCD, which inside one kernel would take an L2 write-back per item);
+//   * when every context fits one partition the grid is (sequence, kv head);
+//     otherwise a one-workgroup plan kernel lists the (sequence, partition)
+//     items and a persistent grid sized to the chip walks the list.
 // The order of every sum depends only on logical token positions, never on the
-// physical block ids, so the output is bit-identical under any placement or
-// sharing of blocks.
+// physical block ids, so the output is
+// bit-identical under any placement or sharing of blocks and between runs.
 
 #include <math.h>
+
+#include <stdlib.h>
+
+#include <algorithm>
 
 #include "../../include/pa.h"
 #include "pa_internal.h"
@@ -65,14 +76,26 @@ __device__ __forceinline__ float dot_piece(uint4 q, uint4 k, std::false_type /*f
   return s;
 }
 
-// element e of a 16-byte piece as fp32
+// An empty asm that reads x: the compiler must have x loaded here.  Used once
+// before a loop so that loads issued ahead of it are not waited for inside it
+// (the wait counter is in-order: a wait for an old load inside the loop would
+// also wait for the prefetch issued in the same iteration).
+__device__ __forceinline__ void loaded(uint32_t x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void loaded(const uint4& x) {
+  loaded(x.x);
+  loaded(x.y);
+  loaded(x.z);
+  loaded(x.w);
+}
+
+// element e of a 16-byte piece as fp32 (e is a compile-time index after unrolling)
 template <bool BF16>
 __device__ __forceinline__ float piece_elem(const uint4& v, int e) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  const uint32_t w = e < (BF16 ? 2 : 1) ? v.x : e < (BF16 ? 4 : 2) ? v.y : e < (BF16 ? 6 : 3) ? v.z : v.w;
   if constexpr (BF16) {
-    return (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
+    return (e & 1) ? bf16_hi(w) : bf16_lo(w);
   } else {
-    return __uint_as_float(w[e]);
+    return __uint_as_float(w);
   }
 }
 
@@ -85,8 +108,9 @@ __device__ __forceinline__ void store_elem(void* base, int64_t idx, float x) {
   }
 }
 
-// Resolve the row of q/out and the attended length for workgroup's sequence.
-// Returns false when this sequence is not handled by the decode kernels.
+// The row of q/out and the attended length of a sequence.  Returns false when
+// the sequence is not served by the decode kernels (a multi-token chunk of a
+// packed batch).
 template <bool VARLEN>
 __device__ __forceinline__ bool decode_row(const DecodeArgs& a, int seq, int& qrow, int& ctx) {
   if constexpr (VARLEN) {
@@ -102,8 +126,21 @@ __device__ __forceinline__ bool decode_row(const DecodeArgs& a, int seq, int& qr
   return true;
 }
 
-template <bool BF16, int D, int G, bool VARLEN>
-__global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
+__device__ __forceinline__ int parts_of(int ctx, int part_tokens) {
+  return max(1, ceil_div(ctx, part_tokens));
+}
+
+template <int G, int D>
+struct DecodeShared {
+  float ml[kDecodeMaxWaves][G][2];
+  float acc[kDecodeMaxWaves][G][D];
+};
+
+// One work item: partition `part` of sequence `seq`, kv head `kvh`.  NB
+// register buffers per wave: NB - 1 blocks stay in flight while one is consumed.
+template <bool BF16, int D, int G, bool VARLEN, int NB>
+__device__ __forceinline__ void decode_item(const DecodeArgs& a, int seq, int part, int kvh,
+                                            DecodeShared<G, D>& sm) {
   using IsBF16 = std::integral_constant<bool, BF16>;
   constexpr int EB = BF16 ? 2 : 4;
   constexpr int EPL = 16 / EB;              // elements in a lane's 16-byte piece
@@ -111,37 +148,44 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
   constexpr int TPL = 64 / LPT;             // token rows per wave-wide load
   constexpr int NLD = kBlockSize / TPL;     // wave-wide loads per 16-token tile
   constexpr int TILE_PIECES = kBlockSize * LPT;
+  constexpr int NS = NLD * G;               // scores per lane per tile
   static_assert(LPT == 8 || LPT == 16 || LPT == 32, "piece layout");
   constexpr float kNegInf = -INFINITY;
 
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int seq = blockIdx.z;
-  int qrow, ctx;
-  if (!decode_row<VARLEN>(a, seq, qrow, ctx)) return;
-  const int nparts = max(1, ceil_div(ctx, kPartitionTokens));
-  if (part >= nparts) return;
-
-  const int tok0 = part * kPartitionTokens;
-  const int tok1 = min(ctx, tok0 + kPartitionTokens);
-  const int nblk = tok1 > tok0 ? ceil_div(tok1 - tok0, kBlockSize) : 0;
-  const int32_t* table =
-      a.block_tables + (int64_t)seq * a.max_blocks_per_seq + tok0 / kBlockSize;
-
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nwaves = a.waves;
   const int row = lane / LPT;
   const int col = lane % LPT;
   const int hq = a.num_q_heads;
   const int hkv = a.num_kv_heads;
+  const int pt = a.part_tokens;
+  const int tok0 = part * pt;
 
-  // this lane's piece of the g query heads that read kv head `kvh`
+  // Three independent loads go out together: the context length (scalar), this
+  // wave's table entries (lane i: the wave's i-th block of the partition; the
+  // index is clamped into the table row, so entries past the context are
+  // in-bounds garbage that is never used) and the query pieces.
+  const int32_t* table = a.block_tables + (int64_t)seq * a.max_blocks_per_seq + tok0 / kBlockSize;
+  const int row_left = a.max_blocks_per_seq - tok0 / kBlockSize;  // >= 1 for a live item
+  const int my_entry = table[min(wave + nwaves * lane, row_left - 1)];
+  int qrow, ctx;
+  if (!decode_row<VARLEN>(a, seq, qrow, ctx)) return;
+  const int nparts = parts_of(ctx, pt);
+  if (part >= nparts) return;
   uint4 qv[G];
   {
     const uint4* qb = static_cast<const uint4*>(a.q) + ((int64_t)qrow * hq + kvh * G) * LPT + col;
 #pragma unroll
     for (int h = 0; h < G; ++h) qv[h] = qb[h * LPT];
+#pragma unroll
+    for (int h = 0; h < G; ++h) loaded(qv[h]);
+    loaded((uint32_t)my_entry);
   }
+
+  const int tok1 = min(ctx, tok0 + pt);
+  const int nblk = tok1 > tok0 ? ceil_div(tok1 - tok0, kBlockSize) : 0;
+  const int nmine = nblk > wave ? ceil_div(nblk - wave, nwaves) : 0;  // <= 64
 
   float m[G], l[G], acc[G][EPL];
 #pragma unroll
@@ -156,46 +200,53 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
   const uint4* kc = static_cast<const uint4*>(a.k_cache);
   const uint4* vc = static_cast<const uint4*>(a.v_cache);
 
-  auto load = [&](int b, uint4* kr, uint4* vr) -> bool {
-    const int phys = table[b];
-    if (phys < 0 || (int64_t)phys >= a.num_blocks) return false;
-    const int64_t base = ((int64_t)phys * hkv + kvh) * TILE_PIECES + lane;
+  // Loads of the K and V tiles of this wave's i-th block (i clamped to the last
+  // one, so the loop's loads are unconditional and its waits count only the
+  // block it consumes; a repeated last block hits in L2).  An unusable block id
+  // reads block 0's tile, which consume() masks.
+  auto load = [&](int i, uint4 (&kr)[NLD], uint4 (&vr)[NLD]) -> int {
+    const int raw = __builtin_amdgcn_readlane(my_entry, min(i, nmine - 1));
+    const int phys = (raw >= 0 && (int64_t)raw < a.num_blocks) ? raw : -1;
+    const int64_t base = ((int64_t)max(phys, 0) * hkv + kvh) * TILE_PIECES + lane;
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       kr[j] = kc[base + j * 64];
       vr[j] = vc[base + j * 64];
     }
-    return true;
+    return phys;
   };
 
-  auto consume = [&](int b, const uint4* kr, const uint4* vr, bool ok) {
-    const int t_base = tok0 + b * kBlockSize;
-    const bool tail = !ok || (t_base + kBlockSize > tok1);
-    float s[NLD][G];
+  auto consume = [&](int i, int phys, const uint4 (&kr)[NLD], const uint4 (&vr)[NLD]) {
+    const int t_base = tok0 + (wave + nwaves * i) * kBlockSize;
+    float s[NS];
 #pragma unroll
     for (int j = 0; j < NLD; ++j)
 #pragma unroll
-      for (int h = 0; h < G; ++h) s[j][h] = group_sum<LPT>(dot_piece(qv[h], kr[j], IsBF16{})) * sl2;
+      for (int h = 0; h < G; ++h) s[j * G + h] = dot_piece(qv[h], kr[j], IsBF16{});
+    group_sum_n<LPT, NS>(s);
+#pragma unroll
+    for (int k = 0; k < NS; ++k) s[k] *= sl2;
     uint4 vv[NLD];
 #pragma unroll
     for (int j = 0; j < NLD; ++j) vv[j] = vr[j];
-    if (tail) {
-      // select, never multiply: stale slots may hold NaN
+    if (phys < 0 || t_base + kBlockSize > tok1) {
+      // a tail or unusable block: select, never multiply -- stale slots may hold NaN
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
-        const bool valid = ok && (t_base + row + j * TPL < tok1);
+        const bool valid = phys >= 0 && (t_base + row + j * TPL < tok1);
         if (!valid) {
           vv[j] = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-          for (int h = 0; h < G; ++h) s[j][h] = kNegInf;
+          for (int h = 0; h < G; ++h) s[j * G + h] = kNegInf;
         }
       }
     }
+    float p[NS];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float mb = s[0][h];
+      float mb = s[h];
 #pragma unroll
-      for (int j = 1; j < NLD; ++j) mb = fmaxf(mb, s[j][h]);
+      for (int j = 1; j < NLD; ++j) mb = fmaxf(mb, s[j * G + h]);
       const float mn = fmaxf(m[h], mb);
       const float mref = (mn == kNegInf) ? 0.f : mn;
       const float alpha = fast_exp2(m[h] - mref);
@@ -204,33 +255,35 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
       for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
-        const float p = fast_exp2(s[j][h] - mref);
-        l[h] += p;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, piece_elem<BF16>(vv[j], e), acc[h][e]);
+        p[j * G + h] = fast_exp2(s[j * G + h] - mref);
+        l[h] += p[j * G + h];
       }
       m[h] = mn;
     }
+    // each V element is widened once and used by all g heads
+#pragma unroll
+    for (int j = 0; j < NLD; ++j)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float v = piece_elem<BF16>(vv[j], e);
+#pragma unroll
+        for (int h = 0; h < G; ++h) acc[h][e] = fmaf(p[j * G + h], v, acc[h][e]);
+      }
   };
 
-  // blocks wave, wave+4, ...; the next block is in flight while one is consumed
-  {
-    uint4 kb[NLD], vb[NLD];
-    int b = wave;
-    bool ok = false;
-    if (b < nblk) ok = load(b, kb, vb);
-    for (; b < nblk; b += kDecodeWaves) {
-      uint4 kn[NLD], vn[NLD];
-      bool okn = false;
-      const int bn = b + kDecodeWaves;
-      if (bn < nblk) okn = load(bn, kn, vn);
-      consume(b, kb, vb, ok);
+  if (nmine > 0) {
+    // a ring of NB register buffers, all filled before the first wait; the
+    // block consumed from buffer b is replaced by the one NB blocks later
+    uint4 kb[NB][NLD], vb[NB][NLD];
+    int id[NB];
 #pragma unroll
-      for (int j = 0; j < NLD; ++j) {
-        kb[j] = kn[j];
-        vb[j] = vn[j];
+    for (int b = 0; b < NB; ++b) id[b] = load(b, kb[b], vb[b]);
+    for (int i = 0; i < nmine; i += NB) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        if (b == 0 || i + b < nmine) consume(i + b, id[b], kb[b], vb[b]);
+        id[b] = load(i + b + NB, kb[b], vb[b]);
       }
-      ok = okn;
     }
   }
 
@@ -252,96 +305,188 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
     }
   }
 
-  // merge the waves in LDS
-  __shared__ float sm_ml[kDecodeWaves][G][2];
-  __shared__ float sm_acc[kDecodeWaves][G][D];
+  // merge the waves in LDS (the barrier first protects LDS from the previous item)
+  __syncthreads();
   if (row == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) sm_acc[wave][h][col * EPL + e] = acc[h][e];
+      for (int e = 0; e < EPL; ++e) sm.acc[wave][h][col * EPL + e] = acc[h][e];
       if (col == 0) {
-        sm_ml[wave][h][0] = m[h];
-        sm_ml[wave][h][1] = l[h];
+        sm.ml[wave][h][0] = m[h];
+        sm.ml[wave][h][1] = l[h];
       }
     }
   }
   __syncthreads();
 
-  const int64_t part_base = (int64_t)seq * hq + kvh * G;
+  const int64_t row_base = (int64_t)seq * hq + kvh * G;  // (seq, first q head) partial row
   for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
     const int h = idx / D;
     const int d = idx - h * D;
     float mx = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) mx = fmaxf(mx, sm_ml[w][h][0]);
+    for (int w = 0; w < nwaves; ++w) mx = fmaxf(mx, sm.ml[w][h][0]);
     const float mref = (mx == kNegInf) ? 0.f : mx;
     float lsum = 0.f, asum = 0.f;
-#pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) {
-      const float wt = fast_exp2(sm_ml[w][h][0] - mref);
-      lsum += wt * sm_ml[w][h][1];
-      asum += wt * sm_acc[w][h][d];
+    for (int w = 0; w < nwaves; ++w) {
+      const float wt = fast_exp2(sm.ml[w][h][0] - mref);
+      lsum += wt * sm.ml[w][h][1];
+      asum += wt * sm.acc[w][h][d];
     }
     if (nparts == 1) {
-      const float o = lsum > 0.f ? asum / lsum : 0.f;
-      store_elem<BF16>(a.out, ((int64_t)qrow * hq + kvh * G + h) * D + d, o);
+      store_elem<BF16>(a.out, ((int64_t)qrow * hq + kvh * G + h) * D + d,
+                       lsum > 0.f ? asum / lsum : 0.f);
     } else {
-      const int64_t pidx = (part_base + h) * a.max_parts + part;
-      float* ws_ml = a.ws;
-      float* ws_acc = a.ws + (int64_t)a.num_seqs * hq * a.max_parts * 2;
-      ws_acc[pidx * D + d] = asum;
+      const int64_t pidx = (row_base + h) * a.max_parts + part;
+      a.ws.acc[pidx * D + d] = asum;
       if (d == 0) {
-        ws_ml[pidx * 2 + 0] = mx;
-        ws_ml[pidx * 2 + 1] = lsum;
+        a.ws.ml[pidx * 2 + 0] = mx;
+        a.ws.ml[pidx * 2 + 1] = lsum;
       }
     }
   }
 }
 
 // Merge the partitions of one (sequence, q head): weights 2^(m_p - max m) in
-// ascending partition order.
+// ascending partition order.  Runs after the partition kernel on the same
+// stream; the kernel boundary makes the partials visible.
 template <bool BF16, int D, bool VARLEN>
-__global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
   constexpr float kNegInf = -INFINITY;
   const int h = blockIdx.x;
   const int seq = blockIdx.y;
   int qrow, ctx;
   if (!decode_row<VARLEN>(a, seq, qrow, ctx)) return;
-  const int nparts = max(1, ceil_div(ctx, kPartitionTokens));
+  const int nparts = parts_of(ctx, a.part_tokens);
   if (nparts <= 1) return;
   const int hq = a.num_q_heads;
   const int d = threadIdx.x;
-  const int64_t pbase = ((int64_t)seq * hq + h) * a.max_parts;
-  const float* ws_ml = a.ws + pbase * 2;
-  const float* ws_acc = a.ws + (int64_t)a.num_seqs * hq * a.max_parts * 2 + pbase * D;
+  const int64_t prow = ((int64_t)seq * hq + h) * a.max_parts;
+  const float* ml = a.ws.ml + prow * 2;
+  const float* pacc = a.ws.acc + prow * D + d;
   float mx = kNegInf;
-  for (int p = 0; p < nparts; ++p) mx = fmaxf(mx, ws_ml[2 * p]);
+  for (int p = 0; p < nparts; ++p) mx = fmaxf(mx, ml[2 * p]);
   const float mref = (mx == kNegInf) ? 0.f : mx;
   float lsum = 0.f, asum = 0.f;
   for (int p = 0; p < nparts; ++p) {
-    const float wt = fast_exp2(ws_ml[2 * p] - mref);
-    lsum += wt * ws_ml[2 * p + 1];
-    asum += wt * ws_acc[p * D + d];
+    const float wt = fast_exp2(ml[2 * p] - mref);
+    lsum += wt * ml[2 * p + 1];
+    asum += wt * pacc[(int64_t)p * D];
   }
-  const float o = lsum > 0.f ? asum / lsum : 0.f;
-  store_elem<BF16>(a.out, ((int64_t)qrow * hq + h) * D + d, o);
+  store_elem<BF16>(a.out, ((int64_t)qrow * hq + h) * D + d, lsum > 0.f ? asum / lsum : 0.f);
 }
 
-template <bool BF16, int D, int G, bool VARLEN>
+// Every context fits one partition: one workgroup per (sequence, kv head).
+template <bool BF16, int D, int G, bool VARLEN, int NB>
+__global__ __launch_bounds__(256) void decode_direct_kernel(DecodeArgs a) {
+  __shared__ DecodeShared<G, D> sm;
+  decode_item<BF16, D, G, VARLEN, NB>(a, blockIdx.x, 0, blockIdx.y, sm);
+}
+
+// Persistent workgroups walk the (sequence, partition) list for kv head blockIdx.y.
+template <bool BF16, int D, int G, bool VARLEN, int NB>
+__global__ __launch_bounds__(256) void decode_list_kernel(DecodeArgs a) {
+  __shared__ DecodeShared<G, D> sm;
+  const int total = *a.ws.count;
+  for (int it = blockIdx.x; it < total; it += gridDim.x) {
+    const int2 w = a.ws.items[it];
+    decode_item<BF16, D, G, VARLEN, NB>(a, w.x, w.y, blockIdx.y, sm);
+  }
+}
+
+// One workgroup: count each sequence's partitions, prefix-sum them, write the
+// (sequence, partition) list in sequence order.
+template <bool VARLEN>
+__global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a) {
+  __shared__ int scan[1024];
+  const int n = a.num_seqs;
+  const int t = threadIdx.x;
+  const int chunk = ceil_div(n, (int)blockDim.x);
+  const int s0 = min(n, t * chunk);
+  const int s1 = min(n, s0 + chunk);
+  int mine = 0;
+  for (int s = s0; s < s1; ++s) {
+    int qrow, ctx;
+    if (decode_row<VARLEN>(a, s, qrow, ctx)) mine += parts_of(ctx, a.part_tokens);
+  }
+  scan[t] = mine;
+  __syncthreads();
+  for (int off = 1; off < (int)blockDim.x; off <<= 1) {
+    const int add = t >= off ? scan[t - off] : 0;
+    __syncthreads();
+    scan[t] += add;
+    __syncthreads();
+  }
+  int pos = scan[t] - mine;
+  for (int s = s0; s < s1; ++s) {
+    int qrow, ctx;
+    if (!decode_row<VARLEN>(a, s, qrow, ctx)) continue;
+    const int np = parts_of(ctx, a.part_tokens);
+    for (int p = 0; p < np; ++p) a.ws.items[pos++] = make_int2(s, p);
+  }
+  if (t == (int)blockDim.x - 1) *a.ws.count = scan[t];
+}
+
+static int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  return cus;
+}
+
+template <bool BF16, int D, int G, bool VARLEN, int NB>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid(a.max_parts, a.num_kv_heads, a.num_seqs);
-  hipLaunchKernelGGL((decode_partition_kernel<BF16, D, G, VARLEN>), grid, dim3(256), 0, stream, a);
+  const dim3 block(64 * a.waves);
+  if (a.max_parts <= 1) {
+    hipLaunchKernelGGL((decode_direct_kernel<BF16, D, G, VARLEN, NB>),
+                       dim3(a.num_seqs, a.num_kv_heads), block, 0, stream, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((decode_plan_kernel<VARLEN>), dim3(1), dim3(1024), 0, stream, a);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || a.max_parts <= 1) return err;
-  hipLaunchKernelGGL((decode_reduce_kernel<BF16, D, VARLEN>), dim3(a.num_q_heads, a.num_seqs),
+  if (err != hipSuccess) return err;
+  static int per_cu[kDecodeMaxWaves + 1] = {0, 0, 0, 0, 0};
+  if (per_cu[a.waves] == 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &nb, reinterpret_cast<const void*>(&decode_list_kernel<BF16, D, G, VARLEN, NB>),
+            64 * a.waves, 0) != hipSuccess ||
+        nb <= 0)
+      nb = 2;
+    per_cu[a.waves] = nb;
+  }
+  // twice the resident capacity, so a finished workgroup's slot is refilled
+  const int64_t want = (int64_t)2 * per_cu[a.waves] * device_cus();
+  const int64_t items_bound = (int64_t)a.num_seqs * a.max_parts;
+  const int gx = (int)std::max<int64_t>(
+      1, std::min<int64_t>(items_bound, (want + a.num_kv_heads - 1) / a.num_kv_heads));
+  hipLaunchKernelGGL((decode_list_kernel<BF16, D, G, VARLEN, NB>), dim3(gx, a.num_kv_heads), block,
+                     0, stream, a);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((decode_merge_kernel<BF16, D, VARLEN>), dim3(a.num_q_heads, a.num_seqs),
                      dim3(D), 0, stream, a);
   return hipGetLastError();
 }
 
+template <bool BF16, int D, int G, bool VARLEN>
+static hipError_t launch_buffers(const DecodeArgs& a, hipStream_t s) {
+  if constexpr (BF16 && D == 128) {
+    switch (a.buffers) {
+      case 3: return launch_decode_t<BF16, D, G, VARLEN, 3>(a, s);
+      case 4: return launch_decode_t<BF16, D, G, VARLEN, 4>(a, s);
+      default: return launch_decode_t<BF16, D, G, VARLEN, 2>(a, s);
+    }
+  } else {
+    return launch_decode_t<BF16, D, G, VARLEN, 2>(a, s);
+  }
+}
+
 template <bool BF16, int D, int G>
 static hipError_t launch_mode(const DecodeArgs& a, hipStream_t s) {
-  return a.varlen ? launch_decode_t<BF16, D, G, true>(a, s) : launch_decode_t<BF16, D, G, false>(a, s);
+  return a.varlen ? launch_buffers<BF16, D, G, true>(a, s) : launch_buffers<BF16, D, G, false>(a, s);
 }
 
 template <bool BF16, int D>
@@ -362,6 +507,33 @@ static hipError_t launch_dim(const DecodeArgs& a, hipStream_t s) {
     case 128: return launch_group<BF16, 128>(a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+static int env_int(const char* name, int fallback) {
+  const char* v = getenv(name);
+  if (!v || !*v) return fallback;
+  char* end = nullptr;
+  const long x = strtol(v, &end, 10);
+  return (end && *end == 0) ? (int)x : fallback;
+}
+
+void decode_config(int num_seqs, int num_kv_heads, int max_context_len, int* waves,
+                   int* part_tokens, int* buffers) {
+  (void)num_seqs;
+  (void)num_kv_heads;
+  (void)max_context_len;
+  int w = 4, pt = 512, nb = 2;
+  // tuning overrides; only values that keep every access in bounds are taken
+  const int ew = env_int("PA_DECODE_WAVES", 0);
+  if (ew == 1 || ew == 2 || ew == 4) w = ew;
+  const int ept = env_int("PA_DECODE_PARTITION", 0);
+  if (ept >= kMinPartitionTokens && ept % kBlockSize == 0) pt = ept;
+  if (pt > kBlockSize * kMaxEntriesPerWave * w) pt = kBlockSize * kMaxEntriesPerWave * w;
+  const int enb = env_int("PA_DECODE_BUFFERS", 0);
+  if (enb >= 2 && enb <= 4) nb = enb;
+  *waves = w;
+  *part_tokens = pt;
+  *buffers = nb;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {

@@ -7,9 +7,10 @@
 
 namespace pa {
 
-constexpr int kBlockSize = 16;        // tokens per physical block
-constexpr int kDecodeWaves = 4;       // waves per decode workgroup
-constexpr int kPartitionTokens = 512; // split-K partition (multiple of kBlockSize)
+constexpr int kBlockSize = 16;           // tokens per physical block
+constexpr int kDecodeMaxWaves = 4;       // waves per decode workgroup (1, 2 or 4)
+constexpr int kMinPartitionTokens = 256; // smallest split-K partition; sizes the workspace
+constexpr int kMaxEntriesPerWave = 64;   // table entries a wave holds (one per lane)
 
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -54,11 +55,77 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// The same all-reduce applied to N independent values, one DPP step at a time
+// across all of them, so consecutive DPP operations never depend on each other.
+template <int W, int N>
+__device__ __forceinline__ void group_sum_n(float (&x)[N]) {
+  static_assert(W == 8 || W == 16 || W == 32 || W == 64, "group width");
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] += dpp_f32<0xB1>(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] += dpp_f32<0x4E>(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] += dpp_f32<0x141>(x[i]);
+  if constexpr (W >= 16) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += dpp_f32<0x140>(x[i]);
+  }
+  if constexpr (W >= 32) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += __shfl_xor(x[i], 16);
+  }
+  if constexpr (W >= 64) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] += __shfl_xor(x[i], 32);
+  }
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------
 // launch arguments
 // ---------------------------------------------------------------------------
+
+// Decode workspace (used only when some context spans several partitions):
+//   ml       float [num_seqs][num_q_heads][max_parts][2]  (running max in log2 units, sum)
+//   acc      float [num_seqs][num_q_heads][max_parts][head_dim]
+//   count    int   [1]                       (work items in the list)
+//   items    int2  [num_seqs * max_parts]    ((sequence, partition) work list)
+struct DecodeWorkspace {
+  float* ml;
+  float* acc;
+  int32_t* count;
+  int2* items;
+};
+
+inline int decode_max_parts(int max_context_len, int partition_tokens = kMinPartitionTokens) {
+  return max_context_len <= 0 ? 1 : ceil_div(max_context_len, partition_tokens);
+}
+
+inline size_t decode_ws_bytes(int num_seqs, int num_q_heads, int head_dim, int max_parts) {
+  if (max_parts <= 1) return 0;
+  const size_t rows = (size_t)num_seqs * num_q_heads * max_parts;
+  size_t bytes = rows * 2 * sizeof(float);                    // ml
+  bytes += rows * (size_t)head_dim * sizeof(float);           // acc
+  bytes += 2 * sizeof(int32_t);                               // count (+ pad to 8 bytes)
+  bytes += (size_t)num_seqs * max_parts * sizeof(int2);       // items
+  return bytes;
+}
+
+inline DecodeWorkspace decode_ws_layout(void* base, int num_seqs, int num_q_heads, int head_dim,
+                                        int max_parts) {
+  DecodeWorkspace w{};
+  char* p = static_cast<char*>(base);
+  const size_t rows = (size_t)num_seqs * num_q_heads * max_parts;
+  w.ml = reinterpret_cast<float*>(p);
+  p += rows * 2 * sizeof(float);
+  w.acc = reinterpret_cast<float*>(p);
+  p += rows * (size_t)head_dim * sizeof(float);
+  w.count = reinterpret_cast<int32_t*>(p);
+  p += 2 * sizeof(int32_t);
+  w.items = reinterpret_cast<int2*>(p);
+  return w;
+}
 
 struct DecodeArgs {
   void* out;
@@ -79,20 +146,12 @@ struct DecodeArgs {
   float scale;
   int32_t dtype;                   // PA_F32 / PA_BF16
   bool varlen;                     // rows come from cu_seqlens; only q_len == 1 seqs
-  float* ws;                       // partials (may be null if max_parts == 1)
-  int32_t max_parts;
+  DecodeWorkspace ws;              // valid when max_parts > 1
+  int32_t max_parts;               // partitions of the longest context
+  int32_t part_tokens;             // split-K partition length (multiple of 16 * waves)
+  int32_t waves;                   // waves per workgroup
+  int32_t buffers;                 // K/V register buffers per wave (2..4)
 };
-
-// Split-K partial layout in the workspace:
-//   ml  [num_seqs][num_q_heads][max_parts][2]   (running max in log2 units, sum)
-//   acc [num_seqs][num_q_heads][max_parts][head_dim]
-inline size_t decode_ws_floats(int num_seqs, int num_q_heads, int head_dim, int max_parts) {
-  if (max_parts <= 1) return 0;
-  return (size_t)num_seqs * num_q_heads * max_parts * (head_dim + 2);
-}
-inline int decode_max_parts(int max_context_len) {
-  return max_context_len <= 0 ? 1 : ceil_div(max_context_len, kPartitionTokens);
-}
 
 struct PrefillArgs {
   void* out;
@@ -124,6 +183,10 @@ hipError_t launch_write_kv(const void* key, const void* value, void* k_cache, vo
                            int32_t head_dim, int64_t num_blocks, int32_t elem_bytes,
                            hipStream_t stream);
 
+// Waves per workgroup and partition length for a decode call, from shapes only
+// (so a call's result never depends on where its blocks live).
+void decode_config(int num_seqs, int num_kv_heads, int max_context_len, int* waves,
+                   int* part_tokens, int* buffers);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 // rows per prefill work item and bound on the number of items

@@ -34,11 +34,14 @@ def test_version_and_status_strings():
 
 
 def test_decode_workspace_size():
-    # a context that fits one partition needs no workspace
-    assert L.pa_decode_workspace_size(64, 32, 128, 384, pa.PA_BF16) == 0
-    assert L.pa_decode_workspace_size(64, 32, 128, 512, pa.PA_BF16) == 0
-    # 513 tokens -> 2 partitions of (m, l, acc[128]) per (seq, head)
-    assert L.pa_decode_workspace_size(4, 8, 128, 513, pa.PA_BF16) == 4 * 8 * 2 * 130 * 4
+    # a context that fits the shortest partition (256 tokens) needs no workspace
+    assert L.pa_decode_workspace_size(64, 32, 128, 256, pa.PA_BF16) == 0
+    assert L.pa_decode_workspace_size(64, 32, 128, 257, pa.PA_BF16) > 0
+    # sized for the shortest partition (256 tokens): 513 tokens -> 3 partitions of
+    # (m, l, acc[128]) per (seq, q head), plus the item count and the
+    # (seq, partition) list
+    assert L.pa_decode_workspace_size(4, 8, 128, 513, pa.PA_BF16) == \
+        4 * 8 * 3 * 130 * 4 + 8 + 4 * 3 * 8
     assert L.pa_decode_workspace_size(4, 8, 96, 513, pa.PA_BF16) == 0        # unsupported d
     assert L.pa_varlen_workspace_size(10, 100, 32, 8, 128, 2000, pa.PA_BF16) > 0
     assert L.pa_varlen_workspace_size(10, 100, 32, 8, 128, 2000, pa.PA_F32) == 0
@@ -60,6 +63,7 @@ def _decode(**over):
     (dict(hq=32, hkv=2), 2), (dict(n=-1), 3), (dict(maxb=0), 3), (dict(maxctx=-5), 3),
     (dict(nblocks=0), 3), (dict(q=None), 1), (dict(bt=None), 1), (dict(out=None), 1),
     (dict(maxctx=4000, wsb=10), 4), (dict(maxctx=4000, wsb=1 << 30), 1),
+    (dict(maxctx=300, wsb=0), 4),
     (dict(n=0, q=None), 0),
 ])
 def test_decode_host_errors(over, status):

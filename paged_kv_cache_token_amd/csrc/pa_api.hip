@@ -120,7 +120,8 @@ int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_c
   a.scale = scale;
   a.dtype = dtype;
   a.varlen = false;
-  decode_config(num_seqs, num_kv_heads, max_context_len, &a.waves, &a.part_tokens, &a.buffers);
+  decode_config(num_seqs, num_kv_heads, max_context_len, &a.waves, &a.part_tokens, &a.buffers,
+                &a.grid_mode, &a.oversub);
   a.max_parts = decode_max_parts(max_context_len, a.part_tokens);
   if (a.max_parts > 1)
     a.ws = decode_ws_layout(workspace, num_seqs, num_q_heads, head_dim, a.max_parts);
@@ -181,7 +182,8 @@ int32_t pa_varlen_prefill(void* out, const void* q, const void* k_cache, const v
   a.scale = scale;
   a.dtype = dtype;
   a.varlen = true;
-  decode_config(num_seqs, num_kv_heads, max_context_len, &a.waves, &a.part_tokens, &a.buffers);
+  decode_config(num_seqs, num_kv_heads, max_context_len, &a.waves, &a.part_tokens, &a.buffers,
+                &a.grid_mode, &a.oversub);
   a.max_parts = decode_max_parts(max_context_len, a.part_tokens);
   if (a.max_parts > 1) a.ws = decode_ws_layout(ws, num_seqs, num_q_heads, head_dim, a.max_parts);
   hipError_t err = launch_decode(a, s);

@@ -108,6 +108,62 @@ __device__ __forceinline__ void store_elem(void* base, int64_t idx, float x) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// DPP row (16-lane) helpers for the one-score-per-lane softmax
+// ---------------------------------------------------------------------------
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// one halving step of a reduce-scatter across lane pairs that differ in BIT
+template <int CTRL, int BIT, int L, int NS>
+__device__ __forceinline__ void rs_step(float (&x)[NS], int c) {
+  if constexpr (L >= 2) {
+    constexpr int H = L / 2;
+    const bool hi = (c & BIT) != 0;
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+      const float send = hi ? x[i] : x[i + H];
+      const float keep = hi ? x[i + H] : x[i];
+      x[i] = keep + dpp_f32<CTRL>(send);
+    }
+  } else {
+    x[0] += dpp_f32<CTRL>(x[0]);
+  }
+}
+
+// Reduce-scatter inside each 16-lane DPP row.  On entry x[0..NS) are a lane's
+// partial sums; on exit x[0..V), V = max(1, NS/16), are complete sums, and lane
+// c of the row holds index c*V + u (NS >= 16) or c / (16/NS) (NS < 16, each
+// index then held by 16/NS lanes).  Partners: row mirror (c <-> 15-c) splits
+// on bit 3, half-row mirror on bit 2, quad swaps on bits 1 and 0.
+template <int NS>
+__device__ __forceinline__ void row_reduce_scatter(float (&x)[NS], int c) {
+  rs_step<0x140, 8, NS, NS>(x, c);
+  rs_step<0x141, 4, (NS / 2 > 1 ? NS / 2 : 1), NS>(x, c);
+  rs_step<0x4E, 2, (NS / 4 > 1 ? NS / 4 : 1), NS>(x, c);
+  rs_step<0xB1, 1, (NS / 8 > 1 ? NS / 8 : 1), NS>(x, c);
+}
+
+// value of lane LANE of the caller's 16-lane row
+template <int LANE>
+__device__ __forceinline__ float row_bcast(float x) { return dpp_f32<0x150 + LANE>(x); }
+
+// max / sum over the 4 lanes {c, c+4, c+8, c+12} (mod 16) of a row
+__device__ __forceinline__ float row_max4(float x) {
+  x = fmaxf(x, dpp_f32<0x124>(x));  // row_ror:4
+  return fmaxf(x, dpp_f32<0x128>(x));  // row_ror:8
+}
+__device__ __forceinline__ float row_sum4(float x) {
+  x += dpp_f32<0x124>(x);
+  return x + dpp_f32<0x128>(x);
+}
+
 // The row of q/out and the attended length of a sequence.  Returns false when
 // the sequence is not served by the decode kernels (a multi-token chunk of a
 // packed batch).
@@ -216,59 +272,126 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int seq, int pa
     return phys;
   };
 
+  // ---- one-score-per-lane softmax (16-lane rows: bf16 d=128, fp32 d=64) ----
+  // After the reduce-scatter, lane c of row r holds the score(s) of index
+  // k = j*G + h with j = c/4 (token r + 4j of the block) and head h; the
+  // running max and sum are kept per (row, head) value, the p values are
+  // broadcast back to the row for the PV products, and the accumulator is
+  // rescaled only when some running max moved.
+  constexpr bool kScatter = (LPT == 16);
+  constexpr int V = NS >= 16 ? NS / 16 : 1;   // values per lane
+  constexpr int R = NS >= 16 ? 1 : 16 / NS;   // lanes per value
+  float mu[V], lu[V];
+#pragma unroll
+  for (int u = 0; u < V; ++u) {
+    mu[u] = kNegInf;
+    lu[u] = 0.f;
+  }
+
   auto consume = [&](int i, int phys, const uint4 (&kr)[NLD], const uint4 (&vr)[NLD]) {
     const int t_base = tok0 + (wave + nwaves * i) * kBlockSize;
+    const bool tail = phys < 0 || t_base + kBlockSize > tok1;
     float s[NS];
 #pragma unroll
     for (int j = 0; j < NLD; ++j)
 #pragma unroll
       for (int h = 0; h < G; ++h) s[j * G + h] = dot_piece(qv[h], kr[j], IsBF16{});
-    group_sum_n<LPT, NS>(s);
-#pragma unroll
-    for (int k = 0; k < NS; ++k) s[k] *= sl2;
     uint4 vv[NLD];
 #pragma unroll
     for (int j = 0; j < NLD; ++j) vv[j] = vr[j];
-    if (phys < 0 || t_base + kBlockSize > tok1) {
-      // a tail or unusable block: select, never multiply -- stale slots may hold NaN
+    if (tail) {
+      // select, never multiply: stale slots may hold NaN
 #pragma unroll
-      for (int j = 0; j < NLD; ++j) {
-        const bool valid = phys >= 0 && (t_base + row + j * TPL < tok1);
-        if (!valid) {
-          vv[j] = make_uint4(0u, 0u, 0u, 0u);
+      for (int j = 0; j < NLD; ++j)
+        if (!(phys >= 0 && (t_base + row + j * TPL < tok1))) vv[j] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    if constexpr (kScatter) {
+      row_reduce_scatter<NS>(s, col);
+      const int jl = col >> 2;  // this lane's token group
+      const bool valid = !tail || (phys >= 0 && (t_base + row + jl * TPL < tok1));
+      float su[V], mn[V];
+      bool moved = false;
 #pragma unroll
-          for (int h = 0; h < G; ++h) s[j * G + h] = kNegInf;
+      for (int u = 0; u < V; ++u) {
+        su[u] = valid ? s[u] * sl2 : kNegInf;
+        mn[u] = fmaxf(mu[u], row_max4(su[u]));
+        moved |= (mn[u] != mu[u]);
+      }
+      if (__any(moved)) {
+        float al[V];
+#pragma unroll
+        for (int u = 0; u < V; ++u) {
+          const float mref = (mn[u] == kNegInf) ? 0.f : mn[u];
+          al[u] = fast_exp2(mu[u] - mref);
+          lu[u] *= al[u];
+          mu[u] = mn[u];
         }
+        static_for<0, G>([&](auto hc) {
+          constexpr int h = decltype(hc)::value;
+          const float ah = row_bcast<(NS >= 16 ? h / V : h * R)>(al[NS >= 16 ? h % V : 0]);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] *= ah;
+        });
       }
+      float pu[V];
+#pragma unroll
+      for (int u = 0; u < V; ++u) {
+        const float mref = (mu[u] == kNegInf) ? 0.f : mu[u];
+        pu[u] = fast_exp2(su[u] - mref);
+        lu[u] += pu[u];
+      }
+      float p[NS];
+      static_for<0, NS>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        p[k] = row_bcast<(NS >= 16 ? k / V : k * R)>(pu[NS >= 16 ? k % V : 0]);
+      });
+#pragma unroll
+      for (int j = 0; j < NLD; ++j)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          const float v = piece_elem<BF16>(vv[j], e);
+#pragma unroll
+          for (int h = 0; h < G; ++h) acc[h][e] = fmaf(p[j * G + h], v, acc[h][e]);
+        }
+    } else {
+      group_sum_n<LPT, NS>(s);
+#pragma unroll
+      for (int k = 0; k < NS; ++k) s[k] *= sl2;
+      if (tail) {
+#pragma unroll
+        for (int j = 0; j < NLD; ++j)
+          if (!(phys >= 0 && (t_base + row + j * TPL < tok1)))
+#pragma unroll
+            for (int h = 0; h < G; ++h) s[j * G + h] = kNegInf;
+      }
+      float p[NS];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float mb = s[h];
+#pragma unroll
+        for (int j = 1; j < NLD; ++j) mb = fmaxf(mb, s[j * G + h]);
+        const float mn = fmaxf(m[h], mb);
+        const float mref = (mn == kNegInf) ? 0.f : mn;
+        const float alpha = fast_exp2(m[h] - mref);
+        l[h] *= alpha;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) {
+          p[j * G + h] = fast_exp2(s[j * G + h] - mref);
+          l[h] += p[j * G + h];
+        }
+        m[h] = mn;
+      }
+#pragma unroll
+      for (int j = 0; j < NLD; ++j)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          const float v = piece_elem<BF16>(vv[j], e);
+#pragma unroll
+          for (int h = 0; h < G; ++h) acc[h][e] = fmaf(p[j * G + h], v, acc[h][e]);
+        }
     }
-    float p[NS];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float mb = s[h];
-#pragma unroll
-      for (int j = 1; j < NLD; ++j) mb = fmaxf(mb, s[j * G + h]);
-      const float mn = fmaxf(m[h], mb);
-      const float mref = (mn == kNegInf) ? 0.f : mn;
-      const float alpha = fast_exp2(m[h] - mref);
-      l[h] *= alpha;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
-#pragma unroll
-      for (int j = 0; j < NLD; ++j) {
-        p[j * G + h] = fast_exp2(s[j * G + h] - mref);
-        l[h] += p[j * G + h];
-      }
-      m[h] = mn;
-    }
-    // each V element is widened once and used by all g heads
-#pragma unroll
-    for (int j = 0; j < NLD; ++j)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const float v = piece_elem<BF16>(vv[j], e);
-#pragma unroll
-        for (int h = 0; h < G; ++h) acc[h][e] = fmaf(p[j * G + h], v, acc[h][e]);
-      }
   };
 
   if (nmine > 0) {
@@ -285,6 +408,19 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int seq, int pa
         id[b] = load(i + b + NB, kb[b], vb[b]);
       }
     }
+  }
+
+  if constexpr (kScatter) {
+    // back to per-head running (max, sum) on every lane of the row
+    float ls[V];
+#pragma unroll
+    for (int u = 0; u < V; ++u) ls[u] = row_sum4(lu[u]);
+    static_for<0, G>([&](auto hc) {
+      constexpr int h = decltype(hc)::value;
+      constexpr int src = NS >= 16 ? h / V : h * R;
+      m[h] = row_bcast<src>(mu[NS >= 16 ? h % V : 0]);
+      l[h] = row_bcast<src>(ls[NS >= 16 ? h % V : 0]);
+    });
   }
 
   // merge the lane groups of this wave (token rows) pairwise
@@ -383,6 +519,14 @@ __global__ __launch_bounds__(256) void decode_direct_kernel(DecodeArgs a) {
   decode_item<BF16, D, G, VARLEN, NB>(a, blockIdx.x, 0, blockIdx.y, sm);
 }
 
+// One workgroup per (sequence, kv head, partition); partitions past a
+// sequence's context exit at once.
+template <bool BF16, int D, int G, bool VARLEN, int NB>
+__global__ __launch_bounds__(256) void decode_grid_kernel(DecodeArgs a) {
+  __shared__ DecodeShared<G, D> sm;
+  decode_item<BF16, D, G, VARLEN, NB>(a, blockIdx.x, blockIdx.z, blockIdx.y, sm);
+}
+
 // Persistent workgroups walk the (sequence, partition) list for kv head blockIdx.y.
 template <bool BF16, int D, int G, bool VARLEN, int NB>
 __global__ __launch_bounds__(256) void decode_list_kernel(DecodeArgs a) {
@@ -394,37 +538,49 @@ __global__ __launch_bounds__(256) void decode_list_kernel(DecodeArgs a) {
   }
 }
 
-// One workgroup: count each sequence's partitions, prefix-sum them, write the
-// (sequence, partition) list in sequence order.
+// One workgroup builds the (sequence, partition) list.  Full-length
+// partitions come first, then each sequence's shorter last partition, both in
+// sequence order: the persistent workgroups take items round-robin, so the
+// expensive items are spread one per workgroup before the short ones fill in.
 template <bool VARLEN>
 __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a) {
-  __shared__ int scan[1024];
+  __shared__ int scan_full[1024];
+  __shared__ int scan_part[1024];
   const int n = a.num_seqs;
   const int t = threadIdx.x;
+  const int pt = a.part_tokens;
   const int chunk = ceil_div(n, (int)blockDim.x);
   const int s0 = min(n, t * chunk);
   const int s1 = min(n, s0 + chunk);
-  int mine = 0;
-  for (int s = s0; s < s1; ++s) {
-    int qrow, ctx;
-    if (decode_row<VARLEN>(a, s, qrow, ctx)) mine += parts_of(ctx, a.part_tokens);
-  }
-  scan[t] = mine;
-  __syncthreads();
-  for (int off = 1; off < (int)blockDim.x; off <<= 1) {
-    const int add = t >= off ? scan[t - off] : 0;
-    __syncthreads();
-    scan[t] += add;
-    __syncthreads();
-  }
-  int pos = scan[t] - mine;
+  int full = 0, partial = 0;
   for (int s = s0; s < s1; ++s) {
     int qrow, ctx;
     if (!decode_row<VARLEN>(a, s, qrow, ctx)) continue;
-    const int np = parts_of(ctx, a.part_tokens);
-    for (int p = 0; p < np; ++p) a.ws.items[pos++] = make_int2(s, p);
+    full += ctx / pt;
+    partial += (ctx % pt != 0 || ctx == 0) ? 1 : 0;
   }
-  if (t == (int)blockDim.x - 1) *a.ws.count = scan[t];
+  scan_full[t] = full;
+  scan_part[t] = partial;
+  __syncthreads();
+  for (int off = 1; off < (int)blockDim.x; off <<= 1) {
+    const int af = t >= off ? scan_full[t - off] : 0;
+    const int ap = t >= off ? scan_part[t - off] : 0;
+    __syncthreads();
+    scan_full[t] += af;
+    scan_part[t] += ap;
+    __syncthreads();
+  }
+  const int total_full = scan_full[blockDim.x - 1];
+  int pos_full = scan_full[t] - full;
+  int pos_part = total_full + scan_part[t] - partial;
+  for (int s = s0; s < s1; ++s) {
+    int qrow, ctx;
+    if (!decode_row<VARLEN>(a, s, qrow, ctx)) continue;
+    const int nf = ctx / pt;
+    for (int p = 0; p < nf; ++p) a.ws.items[pos_full++] = make_int2(s, p);
+    if (ctx % pt != 0 || ctx == 0) a.ws.items[pos_part++] = make_int2(s, nf);
+  }
+  if (t == (int)blockDim.x - 1) *a.ws.count = total_full + scan_part[t];
 }
 
 static int device_cus() {
@@ -444,8 +600,18 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
                        dim3(a.num_seqs, a.num_kv_heads), block, 0, stream, a);
     return hipGetLastError();
   }
+  hipError_t err;
+  if (a.grid_mode) {
+    hipLaunchKernelGGL((decode_grid_kernel<BF16, D, G, VARLEN, NB>),
+                       dim3(a.num_seqs, a.num_kv_heads, a.max_parts), block, 0, stream, a);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((decode_merge_kernel<BF16, D, VARLEN>), dim3(a.num_q_heads, a.num_seqs),
+                       dim3(D), 0, stream, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((decode_plan_kernel<VARLEN>), dim3(1), dim3(1024), 0, stream, a);
-  hipError_t err = hipGetLastError();
+  err = hipGetLastError();
   if (err != hipSuccess) return err;
   static int per_cu[kDecodeMaxWaves + 1] = {0, 0, 0, 0, 0};
   if (per_cu[a.waves] == 0) {
@@ -457,8 +623,8 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
       nb = 2;
     per_cu[a.waves] = nb;
   }
-  // twice the resident capacity, so a finished workgroup's slot is refilled
-  const int64_t want = (int64_t)2 * per_cu[a.waves] * device_cus();
+  // a multiple of the resident capacity, so a finished workgroup's slot is refilled
+  const int64_t want = (int64_t)a.oversub * per_cu[a.waves] * device_cus();
   const int64_t items_bound = (int64_t)a.num_seqs * a.max_parts;
   const int gx = (int)std::max<int64_t>(
       1, std::min<int64_t>(items_bound, (want + a.num_kv_heads - 1) / a.num_kv_heads));
@@ -475,6 +641,7 @@ template <bool BF16, int D, int G, bool VARLEN>
 static hipError_t launch_buffers(const DecodeArgs& a, hipStream_t s) {
   if constexpr (BF16 && D == 128) {
     switch (a.buffers) {
+      case 1: return launch_decode_t<BF16, D, G, VARLEN, 1>(a, s);
       case 3: return launch_decode_t<BF16, D, G, VARLEN, 3>(a, s);
       case 4: return launch_decode_t<BF16, D, G, VARLEN, 4>(a, s);
       default: return launch_decode_t<BF16, D, G, VARLEN, 2>(a, s);
@@ -518,11 +685,13 @@ static int env_int(const char* name, int fallback) {
 }
 
 void decode_config(int num_seqs, int num_kv_heads, int max_context_len, int* waves,
-                   int* part_tokens, int* buffers) {
+                   int* part_tokens, int* buffers, int* grid_mode, int* oversub) {
   (void)num_seqs;
   (void)num_kv_heads;
-  (void)max_context_len;
-  int w = 4, pt = 512, nb = 2;
+  // Measured on MI355X (cold caches): 4 waves, 2 buffers and 512-token
+  // partitions are best up to a few thousand tokens; for very long contexts
+  // 1024-token partitions halve the partial traffic and the item count.
+  int w = 4, pt = max_context_len >= 8192 ? 1024 : 512, nb = 2;
   // tuning overrides; only values that keep every access in bounds are taken
   const int ew = env_int("PA_DECODE_WAVES", 0);
   if (ew == 1 || ew == 2 || ew == 4) w = ew;
@@ -530,10 +699,13 @@ void decode_config(int num_seqs, int num_kv_heads, int max_context_len, int* wav
   if (ept >= kMinPartitionTokens && ept % kBlockSize == 0) pt = ept;
   if (pt > kBlockSize * kMaxEntriesPerWave * w) pt = kBlockSize * kMaxEntriesPerWave * w;
   const int enb = env_int("PA_DECODE_BUFFERS", 0);
-  if (enb >= 2 && enb <= 4) nb = enb;
+  if (enb >= 1 && enb <= 4) nb = enb;
   *waves = w;
   *part_tokens = pt;
   *buffers = nb;
+  *grid_mode = env_int("PA_DECODE_GRID", 0) == 1;
+  const int eo = env_int("PA_DECODE_OVERSUB", 0);
+  *oversub = (eo >= 1 && eo <= 8) ? eo : 4;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {

@@ -151,6 +151,8 @@ struct DecodeArgs {
   int32_t part_tokens;             // split-K partition length (multiple of 16 * waves)
   int32_t waves;                   // waves per workgroup
   int32_t buffers;                 // K/V register buffers per wave (2..4)
+  int32_t grid_mode;               // multi-partition: 1 = (seq, kvh, part) grid, 0 = work list
+  int32_t oversub;                 // persistent grid = oversub x resident workgroups
 };
 
 struct PrefillArgs {
@@ -186,7 +188,7 @@ hipError_t launch_write_kv(const void* key, const void* value, void* k_cache, vo
 // Waves per workgroup and partition length for a decode call, from shapes only
 // (so a call's result never depends on where its blocks live).
 void decode_config(int num_seqs, int num_kv_heads, int max_context_len, int* waves,
-                   int* part_tokens, int* buffers);
+                   int* part_tokens, int* buffers, int* grid_mode, int* oversub);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 // rows per prefill work item and bound on the number of items

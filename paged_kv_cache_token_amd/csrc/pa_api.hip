@@ -111,6 +111,7 @@ int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_c
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.num_seqs = num_seqs;
+  a.q_rows = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;
@@ -151,6 +152,7 @@ int32_t pa_varlen_prefill(void* out, const void* q, const void* k_cache, const v
   if (num_seqs < 0 || total_q_tokens < 0 || max_q_len < 0 || max_context_len < 0 ||
       max_blocks_per_seq <= 0 || num_blocks <= 0)
     return PA_ERR_INVALID_ARGUMENT;
+  if (max_q_len > 1 && head_dim != 128) return PA_ERR_UNSUPPORTED;  // matrix-core path: d = 128
   if (num_seqs == 0 || total_q_tokens == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !cu_seqlens || !context_offsets || !block_tables)
     return PA_ERR_NULL_POINTER;
@@ -173,6 +175,7 @@ int32_t pa_varlen_prefill(void* out, const void* q, const void* k_cache, const v
   a.cu_seqlens = cu_seqlens;
   a.context_offsets = context_offsets;
   a.num_seqs = num_seqs;
+  a.q_rows = total_q_tokens;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;

@@ -172,6 +172,7 @@ __device__ __forceinline__ bool decode_row(const DecodeArgs& a, int seq, int& qr
   if constexpr (VARLEN) {
     const int lo = a.cu_seqlens[seq];
     if (a.cu_seqlens[seq + 1] - lo != 1) return false;
+    if (lo < 0 || lo >= a.q_rows) return false;  // outside q / out: skipped
     qrow = lo;
     ctx = a.context_offsets[seq] + 1;
   } else {

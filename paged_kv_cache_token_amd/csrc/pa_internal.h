@@ -137,6 +137,7 @@ struct DecodeArgs {
   const int32_t* cu_seqlens;       // varlen mode: packed query rows
   const int32_t* context_offsets;  // varlen mode: cached tokens before the row
   int32_t num_seqs;
+  int32_t q_rows;                  // rows of q / out (num_seqs, or total packed rows)
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t head_dim;

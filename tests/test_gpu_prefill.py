@@ -1,0 +1,116 @@
+"""GPU parity of pa_varlen_prefill (packed super-sequence: prefill chunks and
+decode rows) against the oracle, max-abs error <= 2e-2 (bf16 inputs, fp32
+accumulation), plus packing invariance and agreement with pa_decode."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle_side import expected, host_state
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def _device_batch(batch):
+    from device_batch import DeviceBatch
+    return DeviceBatch(batch)
+
+
+def _check(batch, seqs=None):
+    say(batch.name, "n", batch.num_seqs, "total_q", batch.total_q, "max_q", batch.max_q_len,
+        "maxctx", batch.max_context_len, "g", batch.num_q_heads // batch.num_kv_heads)
+    db = _device_batch(batch)
+    out = db.step()
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    hs = host_state(batch)
+    assert np.array_equal(db.slots.cpu().numpy(), hs.new_slots)
+    want = expected(batch, hs, seqs)
+    err = 0.0
+    for i, rows in want.items():
+        lo, hi = int(batch.cu_seqlens[i]), int(batch.cu_seqlens[i + 1])
+        err = max(err, float(np.abs(got[lo:hi] - rows).max()) if rows.size else 0.0)
+    say("max abs err", err)
+    assert err <= TOL, err
+    return db, out
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (16, 4), (32, 4), (16, 8)])
+def test_prefill_chunks_with_context(gpu, hq, hkv):
+    # ragged chunk lengths (q tiles and 64-key tiles with tails), prior context
+    # off and on block / tile edges, a two-token chunk
+    q_lens = [100, 70, 2, 129, 33, 64]
+    ctx = [0, 37, 5, 200, 64, 1000]
+    _check(W.varlen_batch(f"chunks_{hq}_{hkv}", 21, q_lens, ctx, hq, hkv, 128, "bf16"))
+
+
+def test_mixed_rows_small(gpu):
+    # decode rows (q_len 1) interleaved with chunks in one super-sequence
+    q_lens = [1, 45, 1, 1, 300, 1, 17]
+    ctx = [700, 0, 1, 2047, 300, 15, 16]
+    _check(W.varlen_batch("mixed_small", 22, q_lens, ctx, 32, 8, 128, "bf16"))
+
+
+def test_packing_invariance(gpu):
+    """Each sequence's rows are the same whether it is packed with others or alone."""
+    import paged_kv_cache_token_amd as pa
+    q_lens = [1, 96, 1, 40]
+    ctx = [500, 33, 1200, 0]
+    batch = W.varlen_batch("packed", 23, q_lens, ctx, 32, 8, 128, "bf16")
+    db = _device_batch(batch)
+    packed = db.step().clone()
+    for i in range(batch.num_seqs):
+        lo, hi = int(batch.cu_seqlens[i]), int(batch.cu_seqlens[i + 1])
+        cu = torch.tensor([0, hi - lo], dtype=torch.int32, device="cuda")
+        co = db.context_offsets[i:i + 1].contiguous()
+        bt = db.block_tables[i:i + 1].contiguous()
+        solo = pa.varlen_prefill(db.q[lo:hi].contiguous(), db.k_cache, db.v_cache, cu, co, bt,
+                                 hi - lo, int(batch.context_lens[i]), batch.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(solo, packed[lo:hi]), i
+
+
+def test_prefill_rows_match_decode(gpu):
+    """Row j of a chunk after c cached tokens attends what a decode step with
+    context c + j + 1 attends (two kernels: equal within the tolerance)."""
+    import paged_kv_cache_token_amd as pa
+    batch = W.varlen_batch("rows_vs_decode", 24, [77], [150], 32, 8, 128, "bf16")
+    db = _device_batch(batch)
+    pre = db.step().clone()
+    L = 77
+    bt = db.block_tables.expand(L, -1).contiguous()
+    lens = torch.arange(151, 151 + L, dtype=torch.int32, device="cuda")
+    dec = pa.decode(db.q, db.k_cache, db.v_cache, bt, lens, 150 + L, batch.scale)
+    torch.cuda.synchronize()
+    assert float((dec.float() - pre.float()).abs().max()) <= TOL
+
+
+def test_prefill_deterministic(gpu):
+    batch = W.varlen_batch("repeat", 25, [200, 1, 90], [300, 40, 0], 32, 8, 128, "bf16")
+    db = _device_batch(batch)
+    a = db.step().clone()
+    b = db.attend().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_prefill_only_config(gpu):
+    _check(W.prefill_only())
+
+
+def test_mixed_step_full_sampled(gpu):
+    batch = W.mixed_step()
+    n_dec = batch.notes["n_decode_rows"]
+    seqs = list(range(batch.num_seqs - batch.notes["n_prefill"], batch.num_seqs))
+    seqs += list(range(0, n_dec, 97))
+    _check(batch, seqs=seqs)

@@ -4,8 +4,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one pass of the whole hot path over one batch: build the new tokens'
-cache slots, store their K/V (pa_build_slot_mapping + pa_write_kv), then the
-attention call (pa_decode, or pa_varlen_prefill for packed workloads).  The
+cache slots, store their K/V and attend.  Decode workloads run it as one
+launch (pa_decode_step: slot, store and attention fused); ``--unfused`` runs
+pa_build_slot_mapping + pa_write_kv + pa_decode instead.  Packed workloads run
+pa_build_slot_mapping + pa_write_kv + pa_varlen_prefill.  The
 default workload is the LLaMA-2-7B-shaped decode batch (64 sequences, contexts
 U[128,384], 32 q = 32 kv heads, head_dim 128, bf16, 16-token blocks from a
 4096-block pool).
@@ -95,6 +97,13 @@ def write_bytes(b) -> int:
     slot_map = 4 * (2 * b.num_seqs + 1) + 4 * b.total_q + 8 * b.total_q
     write = 2 * 2 * b.total_q * row + 8 * b.total_q
     return slot_map + write
+
+
+def fused_write_bytes(b) -> int:
+    """pa_decode_step's store of the new tokens: their K/V read and written,
+    one table entry each."""
+    row = b.num_kv_heads * b.head_dim * b.elem_bytes
+    return 2 * 2 * b.total_q * row + 4 * b.total_q
 
 
 def prefill_flops(b) -> int:
@@ -188,6 +197,8 @@ def main() -> int:
                     help="layer caches to rotate through (0: enough for >= 1 GiB)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="decode: three calls (slot mapping, write, decode) instead of one")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -210,8 +221,10 @@ def main() -> int:
 
     b = make_batch(args.workload)
     kind = "decode" if b.kind == "decode" else "prefill"
+    fused = kind == "decode" and not args.unfused
     att_bytes = attention_bytes(b)
-    wr_bytes = write_bytes(b)
+    # the fused step reads the new K/V rows and stores them: no slot array traffic
+    wr_bytes = fused_write_bytes(b) if fused else write_bytes(b)
     per_layer_ws = att_bytes + wr_bytes
     layers = args.layers or max(1, min(8, math.ceil((1 << 30) / per_layer_ws)))
     dbs = [DeviceBatch(b.with_layer(l), device=dev) for l in range(layers)]
@@ -225,37 +238,57 @@ def main() -> int:
         del src, dst
 
     stream = torch.cuda.current_stream(dev)
+
+    def run_step(d, ev_pair=None):
+        if fused:
+            if ev_pair:
+                ev_pair[0].record(stream)
+            d.fused_step()
+            if ev_pair:
+                ev_pair[1].record(stream)
+            return
+        d.write_new()
+        if ev_pair:
+            ev_pair[0].record(stream)
+        d.attend()
+        if ev_pair:
+            ev_pair[1].record(stream)
+
     for s in range(args.warmup):
-        dbs[s % layers].step()
+        run_step(dbs[s % layers])
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps, synchronized on both sides; HIP events on the
-    # launch stream bracket every attention call
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # timed region 1: exactly K steps, synchronized on both sides, events only at
+    # its ends -> ms_per_step and value
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
     for s in range(args.steps):
-        d = dbs[s % layers]
-        d.write_new()
-        ev[s][0].record(stream)
-        d.attend()
-        ev[s][1].record(stream)
+        run_step(dbs[s % layers])
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_total = t_start.elapsed_time(t_end)
     ms_per_step = ms_total / args.steps
+
+    # timed region 2: the same K steps with a HIP event pair around every
+    # attention launch, on its launch stream -> the kernel's average duration
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        run_step(dbs[s % layers], ev[s])
+    torch.cuda.synchronize()
     att_ms = [a.elapsed_time(z) for a, z in ev]
     att_avg_ms = float(np.mean(att_ms))
 
     step_bytes = att_bytes + wr_bytes
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     if kind == "decode" or args.workload == "mixed_step":
-        achieved = att_bytes / (att_avg_ms * 1e-3) / 1e9
+        kern_bytes = att_bytes + (wr_bytes if fused else 0)
+        achieved = kern_bytes / (att_avg_ms * 1e-3) / 1e9
         traffic = traffic_from_profiles(args.workload, "decode")
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -302,6 +335,9 @@ def main() -> int:
         "cpu_baseline": cpu,
         "seq_steps_per_s": round(b.num_seqs / (ms_per_step * 1e-3), 1),
         "attention_call_us": round(att_avg_ms * 1e3, 2),
+        "step_calls": "pa_decode_step (fused)" if fused else (
+            "pa_build_slot_mapping + pa_write_kv + " +
+            ("pa_decode" if kind == "decode" else "pa_varlen_prefill")),
         "attention_bytes": att_bytes,
         "write_bytes": wr_bytes,
         "step_bytes": step_bytes,

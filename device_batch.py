@@ -79,6 +79,16 @@ class DeviceBatch:
                                  b.max_context_len, b.scale, out=out, workspace=self.workspace)
 
     def step(self) -> torch.Tensor:
-        """One pass of the hot path: slots + write of the new tokens, attention."""
+        """One pass of the hot path: slots + write of the new tokens, attention
+        (three calls)."""
         self.write_new()
         return self.attend()
+
+    def fused_step(self, out: torch.Tensor | None = None) -> torch.Tensor:
+        """The same decode step in one launch (pa_decode_step)."""
+        b = self.b
+        assert b.kind == "decode"
+        out = self.out if out is None else out
+        return pa.decode_step(self.q, self.k_new, self.v_new, self.k_cache, self.v_cache,
+                              self.block_tables, self.context_lens, b.max_context_len, b.scale,
+                              out=out, workspace=self.workspace)

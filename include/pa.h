@@ -164,6 +164,31 @@ int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_c
                   size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_step -- one decode step in a single launch: store each sequence's
+ * new token and attend ([KW] §1.3: store the new token's K/V into its block,
+ * then gather through the block table; the same result as pa_build_slot_mapping
+ * + pa_write_kv + pa_decode, fused so that the step pays one launch).
+ *
+ *   key, value       in   [num_seqs][num_kv_heads][head_dim]: the new token of
+ *                         sequence i, at position context_lens[i] - 1
+ *   k_cache, v_cache in/out  the new token is stored into slot
+ *                         block_tables[i][(ctx-1)/16] * 16 + (ctx-1) % 16
+ *   other arguments  as pa_decode (context_lens includes the new token;
+ *                         workspace size from pa_decode_workspace_size)
+ *
+ * The new token's K/V take part in the attention from the inputs, so the
+ * result does not depend on when the store becomes visible.  A sequence whose
+ * slot block id is outside the pool gets no store.
+ */
+int32_t pa_decode_step(void* out, const void* q, const void* key, const void* value,
+                       void* k_cache, void* v_cache, const int32_t* block_tables,
+                       const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int32_t max_blocks_per_seq, int32_t max_context_len, int64_t num_blocks,
+                       float scale, int32_t dtype, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
  * Bytes of device workspace pa_varlen_prefill needs for these shapes.
  */
 size_t pa_varlen_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32_t num_q_heads,
@@ -191,7 +216,8 @@ size_t pa_varlen_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32_
  * already be in the cache (pa_write_kv first).  Row j of sequence i attends
  * keys 0 .. context_offsets[i] + j of its own sequence (causal, its own key
  * included).  Rows of single-token sequences take the decode kernels; longer
- * chunks take the matrix-core prefill kernel.  Element type: PA_BF16.
+ * chunks take the matrix-core prefill kernel.  Element type: PA_BF16; chunks
+ * of two or more rows need head_dim 128 (PA_ERR_UNSUPPORTED otherwise).
  */
 int32_t pa_varlen_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* cu_seqlens, const int32_t* context_offsets,

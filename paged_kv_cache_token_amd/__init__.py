@@ -4,7 +4,7 @@ Argument marshalling only: every step of the computation runs in the HIP
 kernels behind ``include/pa.h``.  Tensors are PyTorch device tensors; calls are
 enqueued on the current torch stream of the tensors' device and return without
 waiting.  Importing this package fails loudly when libpa.so has not been built
-(``python -m paged_kv_cache_token_amd.build``); there is no fallback path.
+(``python paged_kv_cache_token_amd/build.py``); there is no fallback path.
 """
 from __future__ import annotations
 
@@ -34,6 +34,9 @@ _SIGNATURES = {
     "pa_decode_workspace_size": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "pa_decode": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32,
                            _c_i32, _c_i32, _c_i32, _c_i64, _c_f32, _c_i32, _c_p, _c_sz, _c_p]),
+    "pa_decode_step": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32,
+                                _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_f32, _c_i32,
+                                _c_p, _c_sz, _c_p]),
     "pa_varlen_workspace_size": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "pa_varlen_prefill": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32,
                                    _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
@@ -44,7 +47,7 @@ _SIGNATURES = {
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built: run `python -m paged_kv_cache_token_amd.build` "
+            f"{LIB_PATH} is not built: run `python paged_kv_cache_token_amd/build.py` "
             "(hipcc --offload-arch=gfx950). The library has no non-HIP fallback.")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in _SIGNATURES.items():
@@ -191,6 +194,38 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     return out
 
 
+def decode_step(q: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                context_lens: torch.Tensor, max_context_len: int, scale: float | None = None,
+                out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Store each sequence's new token and attend, in one launch (pa_decode_step)."""
+    for t, nm in ((q, "q"), (key, "key"), (value, "value"), (k_cache, "k_cache"),
+                  (v_cache, "v_cache")):
+        _need(t, nm)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    num_blocks, hkv, bs, d = _cache_dims(k_cache)
+    n, hq, dq = q.shape
+    if dq != d or q.dtype not in _DTYPES or len({q.dtype, key.dtype, value.dtype, k_cache.dtype,
+                                                 v_cache.dtype}) != 1:
+        raise ValueError("q / key / value / cache head_dim or dtype mismatch")
+    if key.shape != (n, hkv, d) or value.shape != key.shape:
+        raise ValueError("key/value must be [num_seqs, num_kv_heads, head_dim]")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype)
+    scale = float(d ** -0.5 if scale is None else scale)
+    size = decode_workspace_size(n, hq, d, max_context_len, q.dtype)
+    workspace, ws_bytes = _workspace(size, q, workspace)
+    _check("pa_decode_step", lib.pa_decode_step(
+        _ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_tables), _ptr(context_lens), n, hq, hkv, d, bs, block_tables.shape[1],
+        int(max_context_len), num_blocks, scale, _DTYPES[q.dtype], _ptr(workspace), ws_bytes,
+        _stream(q)))
+    return out
+
+
 def varlen_workspace_size(num_seqs: int, total_q_tokens: int, num_q_heads: int,
                           num_kv_heads: int, head_dim: int, max_context_len: int,
                           dtype: torch.dtype) -> int:
@@ -229,5 +264,5 @@ def varlen_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
 
 
 __all__ = ["PAError", "PA_F32", "PA_BF16", "BLOCK_SIZE", "build_slot_mapping", "decode",
-           "decode_workspace_size", "header_functions", "lib", "status_string",
+           "decode_step", "decode_workspace_size", "header_functions", "lib", "status_string",
            "varlen_prefill", "varlen_workspace_size", "version", "write_kv"]

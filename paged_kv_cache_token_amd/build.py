@@ -1,6 +1,7 @@
 """Build libpa.so (the paged-attention C ABI) for gfx950 with hipcc, in-tree.
 
-    python -m paged_kv_cache_token_amd.build
+    python paged_kv_cache_token_amd/build.py     (by path: the package itself
+                                                 loads libpa.so on import)
 
 compiles every csrc/*.hip file to an object under _build/ (in parallel) and
 links them into paged_kv_cache_token_amd/libpa.so.  It always recompiles.

@@ -129,6 +129,56 @@ int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_c
   return from_hip(launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
+int32_t pa_decode_step(void* out, const void* q, const void* key, const void* value,
+                       void* k_cache, void* v_cache, const int32_t* block_tables,
+                       const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int32_t max_blocks_per_seq, int32_t max_context_len, int64_t num_blocks,
+                       float scale, int32_t dtype, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(head_dim) || block_size != PA_BLOCK_SIZE ||
+      !heads_ok(num_q_heads, num_kv_heads))
+    return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || num_blocks <= 0)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !key || !value || !k_cache || !v_cache || !block_tables || !context_lens)
+    return PA_ERR_NULL_POINTER;
+  const size_t need =
+      pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, dtype);
+  if (workspace_bytes < need) return PA_ERR_WORKSPACE_TOO_SMALL;
+  if (need > 0 && !workspace) return PA_ERR_NULL_POINTER;
+
+  DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.q_rows = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.num_blocks = num_blocks;
+  a.scale = scale;
+  a.dtype = dtype;
+  a.varlen = false;
+  a.key_new = key;
+  a.value_new = value;
+  a.k_cache_w = k_cache;
+  a.v_cache_w = v_cache;
+  decode_config(num_seqs, num_kv_heads, max_context_len, &a.waves, &a.part_tokens, &a.buffers,
+                &a.grid_mode, &a.oversub);
+  a.max_parts = decode_max_parts(max_context_len, a.part_tokens);
+  if (a.max_parts > 1)
+    a.ws = decode_ws_layout(workspace, num_seqs, num_q_heads, head_dim, a.max_parts);
+  return from_hip(launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t pa_varlen_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32_t num_q_heads,
                                 int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len,
                                 int32_t dtype) {

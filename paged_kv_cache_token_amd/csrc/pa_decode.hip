@@ -231,6 +231,13 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int seq, int pa
   const int nparts = parts_of(ctx, pt);
   if (part >= nparts) return;
   uint4 qv[G];
+  // the new token's K/V (fused step) travel with the query pieces
+  uint4 knew = make_uint4(0u, 0u, 0u, 0u), vnew = knew;
+  if (a.key_new != nullptr) {
+    const int64_t src = ((int64_t)seq * hkv + kvh) * LPT + col;
+    knew = static_cast<const uint4*>(a.key_new)[src];
+    vnew = static_cast<const uint4*>(a.value_new)[src];
+  }
   {
     const uint4* qb = static_cast<const uint4*>(a.q) + ((int64_t)qrow * hq + kvh * G) * LPT + col;
 #pragma unroll
@@ -238,11 +245,20 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int seq, int pa
 #pragma unroll
     for (int h = 0; h < G; ++h) loaded(qv[h]);
     loaded((uint32_t)my_entry);
+    loaded(knew);
+    loaded(vnew);
   }
 
   const int tok1 = min(ctx, tok0 + pt);
   const int nblk = tok1 > tok0 ? ceil_div(tok1 - tok0, kBlockSize) : 0;
   const int nmine = nblk > wave ? ceil_div(nblk - wave, nwaves) : 0;  // <= 64
+
+  // Fused step: the item holding position ctx-1 uses the new token's K/V from
+  // the inputs instead of re-reading the cache (no read-after-write within the
+  // launch), and stores them into their slot once its loads are issued.
+  const bool fused = a.key_new != nullptr && ctx > 0 && ctx - 1 >= tok0 && ctx - 1 < tok1;
+  const int new_off = (ctx - 1) % kBlockSize;                      // row inside its block
+  const int new_blk = fused ? (ctx - 1 - tok0) / kBlockSize : -1;  // partition-local block
 
   float m[G], l[G], acc[G][EPL];
 #pragma unroll
@@ -300,6 +316,16 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int seq, int pa
     uint4 vv[NLD];
 #pragma unroll
     for (int j = 0; j < NLD; ++j) vv[j] = vr[j];
+    if (fused && wave + nwaves * i == new_blk) {
+      // the new token's row comes from the inputs, not the cache
+#pragma unroll
+      for (int j = 0; j < NLD; ++j)
+        if (row + j * TPL == new_off) {
+          vv[j] = vnew;
+#pragma unroll
+          for (int h = 0; h < G; ++h) s[j * G + h] = dot_piece(qv[h], knew, IsBF16{});
+        }
+    }
     if (tail) {
       // select, never multiply: stale slots may hold NaN
 #pragma unroll
@@ -408,6 +434,15 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int seq, int pa
         if (b == 0 || i + b < nmine) consume(i + b, id[b], kb[b], vb[b]);
         id[b] = load(i + b + NB, kb[b], vb[b]);
       }
+    }
+  }
+
+  if (fused && wave == 0 && lane < LPT) {
+    const int raw = a.block_tables[(int64_t)seq * a.max_blocks_per_seq + (ctx - 1) / kBlockSize];
+    if (raw >= 0 && (int64_t)raw < a.num_blocks) {
+      const int64_t dst = (((int64_t)raw * hkv + kvh) * kBlockSize + new_off) * LPT + lane;
+      static_cast<uint4*>(a.k_cache_w)[dst] = knew;
+      static_cast<uint4*>(a.v_cache_w)[dst] = vnew;
     }
   }
 

@@ -147,6 +147,10 @@ struct DecodeArgs {
   float scale;
   int32_t dtype;                   // PA_F32 / PA_BF16
   bool varlen;                     // rows come from cu_seqlens; only q_len == 1 seqs
+  const void* key_new;             // fused step: the new token's K [num_seqs][Hkv][d], or null
+  const void* value_new;           // fused step: the new token's V
+  void* k_cache_w;                 // fused step: caches to store the new token into
+  void* v_cache_w;
   DecodeWorkspace ws;              // valid when max_parts > 1
   int32_t max_parts;               // partitions of the longest context
   int32_t part_tokens;             // split-K partition length (multiple of 16 * waves)

@@ -168,3 +168,40 @@ def test_shared_prefix_full_sampled_and_unshared(gpu):
     out_u = _device_batch(W.shared_prefix_decode(unshared=True)).step()
     torch.cuda.synchronize()
     assert torch.equal(out_s, out_u)
+
+
+# ---- the fused decode step ----------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "ragged_f32_128", "ragged_bf16_g4", "llama2", "gqa"])
+def test_fused_step_equals_separate_calls(gpu, name):
+    """pa_decode_step (one launch) = slot mapping + pa_write_kv + pa_decode:
+    bit-identical output and bit-identical pools afterwards."""
+    lens = [1, 2, 15, 16, 17, 100, 511, 512, 513, 1100, 2049]
+    batch = {
+        "tiny": W.tiny_decode,
+        "ragged_f32_128": lambda: W.decode_batch("r1", 31, lens, 8, 2, 128, "f32", pool_factor=1.3),
+        "ragged_bf16_g4": lambda: W.decode_batch("r2", 32, lens, 32, 8, 128, "bf16", pool_factor=1.3),
+        "llama2": W.llama2_decode,
+        "gqa": W.gqa_decode,
+    }[name]()
+    say("fused vs separate", batch.name)
+    a, b = _device_batch(batch), _device_batch(batch)
+    oa = a.step().clone()
+    ob = b.fused_step().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob)
+    assert bits_equal(host_bits(a.k_cache), host_bits(b.k_cache))
+    assert bits_equal(host_bits(a.v_cache), host_bits(b.v_cache))
+
+
+def test_fused_step_against_oracle(gpu):
+    batch = W.decode_batch("fused_oracle", 33, [1, 16, 17, 700, 1500], 16, 4, 128, "bf16",
+                           pool_factor=1.3)
+    db = _device_batch(batch)
+    out = db.fused_step()
+    torch.cuda.synchronize()
+    hs = host_state(batch)
+    assert bits_equal(host_bits(db.k_cache), hs.k_cache)
+    assert bits_equal(host_bits(db.v_cache), hs.v_cache)
+    err = _max_err(out, expected(batch, hs))
+    assert err <= TOL["bf16"], err

@@ -26,9 +26,10 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 size_t varlen_decode_part_bytes(int32_t num_seqs, int32_t hq, int32_t d, int32_t max_ctx) {
   return align_up(decode_ws_bytes(num_seqs, hq, d, decode_max_parts(max_ctx)));
 }
-size_t varlen_work_bytes(int32_t num_seqs, int32_t total_q, int32_t group) {
-  // one count + two ints per item
-  return align_up((size_t)(1 + 2 * prefill_work_capacity(num_seqs, total_q, group)) * sizeof(int32_t));
+size_t varlen_work_bytes(int32_t num_seqs, int32_t total_q, int32_t hkv, int32_t group) {
+  // count and pad, then two ints per item
+  return align_up((size_t)(2 + 2 * (size_t)prefill_work_capacity(num_seqs, total_q, hkv, group)) *
+                  sizeof(int32_t));
 }
 
 }  // namespace
@@ -186,7 +187,7 @@ size_t pa_varlen_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32_
       !heads_ok(num_q_heads, num_kv_heads))
     return 0;
   return varlen_decode_part_bytes(num_seqs, num_q_heads, head_dim, max_context_len) +
-         varlen_work_bytes(num_seqs, total_q_tokens, num_q_heads / num_kv_heads);
+         varlen_work_bytes(num_seqs, total_q_tokens, num_kv_heads, num_q_heads / num_kv_heads);
 }
 
 int32_t pa_varlen_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -262,7 +263,8 @@ int32_t pa_varlen_prefill(void* out, const void* q, const void* k_cache, const v
   p.num_blocks = num_blocks;
   p.scale = scale;
   p.work = reinterpret_cast<int32_t*>(ws + dec_bytes);
-  p.work_cap = prefill_work_capacity(num_seqs, total_q_tokens, num_q_heads / num_kv_heads);
+  p.work_cap =
+      prefill_work_capacity(num_seqs, total_q_tokens, num_kv_heads, num_q_heads / num_kv_heads);
   return from_hip(launch_prefill(p, s));
 }
 

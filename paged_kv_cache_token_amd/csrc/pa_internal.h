@@ -198,7 +198,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 // rows per prefill work item and bound on the number of items
 int prefill_tile_tokens(int group);
-int prefill_work_capacity(int num_seqs, int total_q_tokens, int group);
+int prefill_work_capacity(int num_seqs, int total_q_tokens, int num_kv_heads, int group);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace pa

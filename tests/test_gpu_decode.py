@@ -205,3 +205,34 @@ def test_fused_step_against_oracle(gpu):
     assert bits_equal(host_bits(db.v_cache), hs.v_cache)
     err = _max_err(out, expected(batch, hs))
     assert err <= TOL["bf16"], err
+
+
+@pytest.mark.parametrize("bad_id", [-3, 10 ** 6])
+def test_decode_out_of_pool_block_takes_no_part(gpu, bad_id):
+    """A live table entry outside [0, num_blocks) is an empty block: its 16
+    tokens drop out of the softmax.  Expected: the oracle's attention over
+    the sequence's other tokens."""
+    import oracle
+    lens = [40, 700, 1500]
+    batch = W.decode_batch("bad_block_dec", 27, lens, 32, 8, 128, "bf16")
+    db = _device_batch(batch)
+    db.step()
+    hs = host_state(batch)
+    drop = {0: 1, 1: 20, 2: 50}   # logical block dropped per sequence
+    bt = db.block_tables.clone()
+    for i, j in drop.items():
+        bt[i, j] = bad_id
+    db.block_tables.copy_(bt)
+    got = db.attend().clone()
+    torch.cuda.synchronize()
+    want = np.zeros((len(lens), batch.num_q_heads, batch.head_dim))
+    for i, j in drop.items():
+        n = int(batch.context_lens[i])
+        keep = np.r_[0:16 * j, 16 * (j + 1):n]
+        k = oracle.widen(oracle.gather(hs.k_cache, batch.block_tables[i], n))[keep]
+        v = oracle.widen(oracle.gather(hs.v_cache, batch.block_tables[i], n))[keep]
+        want[i] = oracle.attend(oracle.widen(hs.q[i:i + 1]), k, v, np.array([n - 16]),
+                                batch.scale)[0]
+    err = _max_err(got, want)
+    say("max abs err", err)
+    assert err <= TOL["bf16"], err

@@ -114,3 +114,36 @@ def test_mixed_step_full_sampled(gpu):
     seqs = list(range(batch.num_seqs - batch.notes["n_prefill"], batch.num_seqs))
     seqs += list(range(0, n_dec, 97))
     _check(batch, seqs=seqs)
+
+
+@pytest.mark.parametrize("bad_id", [-3, 10 ** 6])
+def test_out_of_pool_block_takes_no_part(gpu, bad_id):
+    """A live table entry outside [0, num_blocks) is an empty block: its 16
+    tokens drop out of every row's softmax (the documented contract for
+    invalid ids).  Expected: the oracle's attention over the sequence's other
+    tokens, each row seeing 16 fewer keys."""
+    import oracle
+    q_lens, ctx = [90, 1], [70, 300]
+    batch = W.varlen_batch("bad_block", 26, q_lens, ctx, 32, 8, 128, "bf16")
+    db = _device_batch(batch)
+    db.step()
+    hs = host_state(batch)
+    drop = {0: 2, 1: 7}  # logical block dropped per sequence (inside the context)
+    bt = db.block_tables.clone()
+    for i, j in drop.items():
+        bt[i, j] = bad_id
+    db.block_tables.copy_(bt)
+    got = db.attend().float().cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    err = 0.0
+    for i, j in drop.items():
+        n = int(batch.context_lens[i])
+        keep = np.r_[0:16 * j, 16 * (j + 1):n]
+        k = oracle.widen(oracle.gather(hs.k_cache, batch.block_tables[i], n))[keep]
+        v = oracle.widen(oracle.gather(hs.v_cache, batch.block_tables[i], n))[keep]
+        lo, hi = int(batch.cu_seqlens[i]), int(batch.cu_seqlens[i + 1])
+        visible = int(batch.context_offsets[i]) + np.arange(1, hi - lo + 1) - 16
+        want = oracle.attend(oracle.widen(hs.q[lo:hi]), k, v, visible, batch.scale)
+        err = max(err, float(np.abs(got[lo:hi] - want).max()))
+    say("max abs err", err)
+    assert err <= TOL, err

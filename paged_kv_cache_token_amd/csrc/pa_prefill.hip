@@ -49,8 +49,6 @@ constexpr int kPrefillThreads = 64 * kPrefillWaves;
 constexpr int kPrefillRows = 32 * kPrefillWaves;  // (head, token) rows per item
 constexpr int kKeyTile = 64;                 // keys per tile = 4 physical blocks
 constexpr int kSortBuckets = 1024;           // work-list order: key tiles per item (capped)
-constexpr int kKRow = kPrefillD + 8;         // LDS row of K, bf16 elements (padded)
-constexpr int kVRow = kKeyTile + 4;          // LDS row of V^T, bf16 elements (padded)
 
 int prefill_tile_tokens(int group) { return kPrefillRows / group; }
 
@@ -77,6 +75,7 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(PrefillArgs a, int t
   const int t = threadIdx.x;
   const int maxk = max(0, min(a.max_context_len, a.max_blocks_per_seq * kBlockSize));
   for (int i = t; i < kSortBuckets; i += blockDim.x) count[i] = 0;
+  if (t < 16) a.zero_row[t] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
   auto bucket = [&](int s, int q) {
     const int len = a.cu_seqlens[s + 1] - a.cu_seqlens[s];
@@ -120,29 +119,39 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(PrefillArgs a, int t
   }
 }
 
-// LDS tiles typed by their access width (16-byte K pieces, 4-byte key pairs
-// of V^T) so that every access is provably aligned.
+// LDS tiles: 64 keys x 128 dims of bf16, as [block of 16 keys][16-byte chunk
+// of 8 dims][key in block], the key position XOR-swizzled by the chunk:
+// key k16 of chunk c sits at position k16 ^ 4 (c % 4).  The direct HBM->LDS
+// loads write each wave instruction's 1 KiB contiguously (4 chunks x 16 keys
+// of one block); the 16-byte K reads of 16 keys at one chunk, and the
+// transposing 8-byte V reads of 4 keys x 4 chunks, hit distinct banks.
 struct __attribute__((aligned(16))) PrefillShared {
-  uint4 k[2][kKeyTile][kKRow / 8];      // double-buffered K tile [key][dim / 8]
-  uint32_t vt[2][kPrefillD][kVRow / 2];  // double-buffered V^T tile [dim][key / 2]
+  uint4 k[3][4][16][16];
+  uint4 v[3][4][16][16];
 };
 
-// pack the low (or high) bf16 halves of two words: (lo of a) | (lo of b) << 16
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
-}
-__device__ __forceinline__ uint32_t word(const uint4& v, int w) {
-  return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w;
-}
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // two fp32 -> packed bf16, round to nearest even (one v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_f32_bf16(float lo, float hi) {
   const f32x2_t f = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+#define PA_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// 16 bytes per lane from global memory straight into LDS: lane i's chunk
+// lands at lds_base + 16 i (lds_base is wave-uniform)
+__device__ __forceinline__ void dma16(const uint4* src, uint4* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, PA_LDS(void, lds_base), 16, 0, 0);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane s supplies the address of 4 consecutive bf16; lane j = 4q + c of the
+// group receives element c of the chunks of lanes q, 4 + q, 8 + q, 12 + q.
+__device__ __forceinline__ uint2 lds_read_tr(const uint16_t* p) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(PA_LDS(i16x4_t, p)));
 }
 
 template <int G>
@@ -191,53 +200,44 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int 
     }
   }
 
-  // tile staging (512 threads): thread tid holds K pieces tid and tid + 512 of
-  // the tile's 4 blocks (a block tile is 256 pieces of 16 bytes), and V of keys
-  // 2*(tid/16), +1 at dims (tid%16)*8 .. +8
-  const uint4* kc = static_cast<const uint4*>(a.k_cache);
-  const uint4* vc = static_cast<const uint4*>(a.v_cache);
-  constexpr int kTilePieces = kBlockSize * D / 8;  // 16-byte pieces per block tile
-  uint4 k0, k1, v0, v1;  // the next tile's K and V pieces, in flight
-  auto block_of = [&](int logical) -> int {
-    const int lb = min(logical, a.max_blocks_per_seq - 1);
-    const int phys = table[lb];
+  // Table entries of a tile, one per lane (lane i & 3: block i & 3 of the
+  // tile), loaded one step ahead with vector loads that land with that step's
+  // tile loads; read back as wave-uniform values, so no scalar load waits on
+  // the in-flight tile loads.  Entries past the table's end are clamped (their
+  // keys lie past the item's end).
+  auto entries = [&](int t) -> int {
+    return table[min(t * 4 + (lane & 3), a.max_blocks_per_seq - 1)];
+  };
+  auto phys_of = [&](int e, int blk) -> int {
+    const int phys = __builtin_amdgcn_readlane(e, blk);
     return (phys >= 0 && (int64_t)phys < a.num_blocks) ? phys : -1;
   };
-  auto k_piece = [&](int tile, int piece) -> uint4 {
-    const int phys = block_of(tile * 4 + piece / kTilePieces);
-    const int64_t base = ((int64_t)max(phys, 0) * hkv + kvh) * kTilePieces;
-    return kc[base + piece % kTilePieces];
-  };
-  auto fetch = [&](int tile) {
-    k0 = k_piece(tile, tid);
-    k1 = k_piece(tile, tid + kPrefillThreads);
-    const int key0 = 2 * (tid >> 4);                 // first of this thread's 2 keys
-    const int phys = block_of(tile * 4 + key0 / kBlockSize);
-    const int64_t base = ((int64_t)max(phys, 0) * hkv + kvh) * kTilePieces +
-                         (key0 % kBlockSize) * (D / 8) + (tid & 15);
-    v0 = vc[base];
-    v1 = vc[base + D / 8];
-    // V of keys past the chunk's end (or in an unusable block) must not reach
-    // the products (p = 0 times a stale NaN is NaN): select zero instead
-    const int key = tile * kKeyTile + key0;
-    if (phys < 0 || key >= kend) v0 = make_uint4(0u, 0u, 0u, 0u);
-    if (phys < 0 || key + 1 >= kend) v1 = make_uint4(0u, 0u, 0u, 0u);
-  };
-  auto stage_k = [&](int buf, int piece, uint4 v) {
-    const int key = (piece / kTilePieces) * kBlockSize + (piece % kTilePieces) / 16;
-    sm.k[buf][key][piece & 15] = v;
-  };
-  auto stage = [&](int buf) {
-    stage_k(buf, tid, k0);
-    stage_k(buf, tid + kPrefillThreads, k1);
-    const int key0 = 2 * (tid >> 4);
-    const int d0 = (tid & 15) * 8;
+  // bit b: block b of the tile is outside the pool (its keys take no part)
+  auto bad_mask = [&](int e) -> int {
+    int bad = 0;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      // dims d0 + 2w (low halves) and d0 + 2w + 1 (high halves) of the 2 keys
-      const uint32_t a0 = word(v0, w), a1 = word(v1, w);
-      sm.vt[buf][d0 + 2 * w][key0 / 2] = pack_lo(a0, a1);
-      sm.vt[buf][d0 + 2 * w + 1][key0 / 2] = pack_hi(a0, a1);
+    for (int b = 0; b < 4; ++b) bad |= (phys_of(e, b) < 0 ? 1 : 0) << b;
+    return bad;
+  };
+  // Loads of tile t into LDS buffer b: wave instruction j = 2*wave + r (of 16
+  // per tensor) moves block j/4 of the tile, chunks 4(j%4) .. +3; lane i takes
+  // chunk +i/16 at key position i%16.  Keys past the item's end or in a block
+  // outside the pool read the zero row instead (V must be finite there: p = 0
+  // times a stale NaN would poison the sum; K is masked).
+  const uint4* kc = static_cast<const uint4*>(a.k_cache);
+  const uint4* vc = static_cast<const uint4*>(a.v_cache);
+  auto issue = [&](int t, int b, int e) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int j = 2 * wave + r;
+      const int blk = j >> 2, c0 = 4 * (j & 3);
+      const int phys = phys_of(e, blk);              // wave-uniform
+      const int ch = c0 + (lane >> 4);
+      const int k16 = (lane & 15) ^ (4 * (ch & 3));
+      const bool ok = phys >= 0 && t * kKeyTile + blk * kBlockSize + k16 < kend;
+      const int64_t row = (((int64_t)max(phys, 0) * hkv + kvh) * kBlockSize + k16) * 16 + ch;
+      dma16(ok ? kc + row : a.zero_row + ch, &sm.k[b][blk][c0][0]);
+      dma16(ok ? vc + row : a.zero_row + ch, &sm.v[b][blk][c0][0]);
     }
   };
 
@@ -249,37 +249,62 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int 
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
   float m = kNegInf, lsum = 0.f;
 
-  // Double-buffered LDS tiles, one barrier per tile: tile t is computed from
-  // LDS buffer t%2 while tile t+1 (already in registers) is staged into the
-  // other buffer and the loads of tile t+2 go out.
-  if (ntiles > 0) {
-    fetch(0);
-    stage(0);
-    if (ntiles > 1) fetch(1);
-  }
-  __syncthreads();
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int buf = tile & 1;
-    // blocks of this tile outside the pool take no part (bit b: block b of 4)
-    int bad = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) bad |= (block_of(tile * 4 + b) < 0 ? 1 : 0) << b;
-    // S^T for the tile's two 32-key halves
-    f32x16_t s[2];
+  // S^T of a tile's two 32-key halves from LDS buffer b
+  auto scores = [&](int b, f32x16_t(&sc)[2]) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[u][r] = 0.f;
+      for (int r = 0; r < 16; ++r) sc[u][r] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, sm.k[buf][32 * u + n][ks * 2 + hi]);
-        s[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[u], 0, 0, 0);
+        const int ch = 2 * ks + hi;
+        const bf16x8_t kf = __builtin_bit_cast(
+            bf16x8_t, sm.k[b][2 * u + (n >> 4)][ch][(n & 15) ^ (4 * (ch & 3))]);
+        sc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc[u], 0, 0, 0);
       }
     }
-    // s[u][4i+j] is the raw score of key tile*64 + 32u + 8i + 4hi + j for this
+  };
+
+  // V^T fragment of k step kb (a multiple of 16) and dims dt*32 .. +32: lane
+  // l = 16g + s supplies dims dt*32 + 16(g%2) + 4(s%4) .. +3 of key
+  // kb + 4(g/2) + s/4 (then of that key + 8); the transposing read hands lane
+  // l the 4 keys of its dim dt*32 + l%32.
+  const int vg = lane >> 4, vs = lane & 15;
+  const int vch = 2 * (vg & 1) + ((vs & 3) >> 1);       // chunk within a 32-dim span
+  auto v_frag = [&](int b, int kb, int dt) -> bf16x8_t {
+    uint2 w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k16 = 4 * (vg >> 1) + (vs >> 2) + 8 * h;
+      const uint16_t* p = reinterpret_cast<const uint16_t*>(
+          &sm.v[b][kb >> 4][4 * dt + vch][k16 ^ (4 * vch)]);
+      w[h] = lds_read_tr(p + 4 * (vs & 1));
+    }
+    return __builtin_bit_cast(bf16x8_t, make_uint4(w[0].x, w[0].y, w[1].x, w[1].y));
+  };
+
+  // One key tile.  Its scores `cur` were computed one step earlier; this
+  // step issues the products of tile t+1 into `nxt` (independent of the
+  // softmax work on `cur`, so the matrix cores run while the vector ALUs do
+  // the exponentials), then O += V^T P^T for tile t.  Three LDS buffers, tile
+  // t in t%3: the loads of tile t+2 go out at the start of step t into the
+  // buffer that held tile t-1, whose last reader finished before the previous
+  // step's barrier, and must land before this step's barrier.  e2 holds the
+  // table entries of tile t+2; bq the bad-block masks of tiles t, t+1 (and
+  // t+2 once added) in 4-bit fields.
+  int e2 = 0, bq = 0;
+  auto step = [&](int t, f32x16_t(&cur)[2], f32x16_t(&nxt)[2]) {
+    const int bc = t % 3;
+    const int bn = bc == 2 ? 0 : bc + 1;
+    const int bs = bn == 2 ? 0 : bn + 1;
+    if (t + 2 < ntiles) issue(t + 2, bs, e2);
+    bq |= bad_mask(e2) << 8;
+    e2 = entries(t + 3);
+    const int bad = bq & 15;
+    // cur[u][4i+j] is the raw score of key t*64 + 32u + 8i + 4hi + j for this
     // row; the running max m is kept in raw units (scale > 0) and the scale
     // is folded into the exponent: p = 2^(s*scale*log2e - m*scale*log2e)
-    const int kt0 = tile * kKeyTile;
+    const int kt0 = t * kKeyTile;
     // every key of the tile visible to every row: no masking
     const bool full = bad == 0 && kt0 + kKeyTile <= full_lim;
     if (!full) {
@@ -293,16 +318,21 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int 
         for (int r = 0; r < 16; ++r) {
           // key kt0 + 32u + 8(r/4) + 4hi + r%4, in block 2u + r/8 of the tile
           if (32 * u + 8 * (r >> 2) + (r & 3) >= lim || ((bad >> (2 * u + (r >> 3))) & 1))
-            s[u][r] = kNegInf;
+            cur[u][r] = kNegInf;
         }
     }
     float mloc = kNegInf;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) mloc = fmaxf(mloc, fmaxf(s[u][r], s[u][r + 1]));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float mn = fmaxf(m, mloc);
+      for (int r = 0; r < 16; r += 2)
+        mloc = __builtin_elementwise_maximum(mloc,
+                                             __builtin_elementwise_maximum(cur[u][r], cur[u][r + 1]));
+    // the row's other 32 keys sit in lane ^ 32
+    const auto mx = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc),
+                                                     false, false);
+    const float mn = __builtin_elementwise_maximum(
+        m, __builtin_elementwise_maximum(__uint_as_float(mx[0]), __uint_as_float(mx[1])));
     if (__any(mn != m)) {
       // some row's max moved: rescale (rows whose max did not move get 1);
       // kept a real branch so tiles that move no max skip the 64 products
@@ -315,6 +345,9 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int 
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
       m = mn;
     }
+    // the next tile's products (past the last tile they read a stale buffer
+    // and are discarded)
+    scores(bn, nxt);
     const float moff = -((m == kNegInf) ? 0.f : m) * sl2;
     float psum = 0.f;
     uint32_t pf[2][2][4];  // P^T fragments: [half u][16-key step t2][packed pairs]
@@ -324,8 +357,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int 
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const float p0 = fast_exp2(fmaf(s[u][8 * t2 + e], sl2, moff));
-          const float p1 = fast_exp2(fmaf(s[u][8 * t2 + e + 1], sl2, moff));
+          const float p0 = fast_exp2(fmaf(cur[u][8 * t2 + e], sl2, moff));
+          const float p1 = fast_exp2(fmaf(cur[u][8 * t2 + e + 1], sl2, moff));
           psum += p0 + p1;
           pf[u][t2][e / 2] = pack_f32_bf16(p0, p1);
         }
@@ -338,24 +371,41 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int 
       for (int t2 = 0; t2 < 2; ++t2) {
         const bf16x8_t pb = __builtin_bit_cast(
             bf16x8_t, make_uint4(pf[u][t2][0], pf[u][t2][1], pf[u][t2][2], pf[u][t2][3]));
-        const int kb = 32 * u + 16 * t2 + 4 * hi;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const uint32_t* vrow = &sm.vt[buf][dt * 32 + n][kb / 2];
-          const bf16x8_t vf =
-              __builtin_bit_cast(bf16x8_t, make_uint4(vrow[0], vrow[1], vrow[4], vrow[5]));
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[dt], 0, 0, 0);
-        }
+        for (int dt = 0; dt < 4; ++dt)
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag(bc, 32 * u + 16 * t2, dt), pb,
+                                                          o[dt], 0, 0, 0);
       }
-    if (tile + 1 < ntiles) {
-      stage(buf ^ 1);
-      if (tile + 2 < ntiles) fetch(tile + 2);
+    bq >>= 4;
+    // this wave's loads of tile t+2 (and the entries of tile t+3) have
+    // landed; the barrier publishes them and frees buffer bc
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  if (ntiles > 0) {
+    const int e0 = entries(0);
+    issue(0, 0, e0);
+    bq = bad_mask(e0);
+    const int e1 = entries(1);
+    if (ntiles > 1) issue(1, 1, e1);
+    bq |= bad_mask(e1) << 4;
+    e2 = entries(2);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    f32x16_t sa[2], sb[2];
+    scores(0, sa);
+    for (int t = 0; t < ntiles; ++t) {
+      step(t, sa, sb);
+      sa[0] = sb[0];
+      sa[1] = sb[1];
     }
-    __syncthreads();  // tile+1 staged for all; everyone is done with buffer `buf`
   }
 
   // this lane summed 32 of each tile's 64 keys; its partner lane^32 the rest
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const auto ls = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum),
+                                                   false, false);
+  const float ltot = __uint_as_float(ls[0]) + __uint_as_float(ls[1]);
   if (valid_q) {
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     uint16_t* out = static_cast<uint16_t*>(a.out) + ((int64_t)(lo_row + q0 + tok) * hq + head) * D;

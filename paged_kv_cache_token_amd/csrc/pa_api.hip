@@ -22,15 +22,14 @@ int32_t from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// varlen workspace = [decode partials][256-byte zero row][prefill work list]
+// varlen workspace = [decode partials][prefill work list]
 size_t varlen_decode_part_bytes(int32_t num_seqs, int32_t hq, int32_t d, int32_t max_ctx) {
   return align_up(decode_ws_bytes(num_seqs, hq, d, decode_max_parts(max_ctx)));
 }
 size_t varlen_work_bytes(int32_t num_seqs, int32_t total_q, int32_t hkv, int32_t group) {
-  // the zero row, then count and pad, then two ints per item
-  return kAlign + align_up((size_t)(2 + 2 * (size_t)prefill_work_capacity(num_seqs, total_q, hkv,
-                                                                           group)) *
-                           sizeof(int32_t));
+  // count and pad, then two ints per item
+  return align_up((size_t)(2 + 2 * (size_t)prefill_work_capacity(num_seqs, total_q, hkv, group)) *
+                  sizeof(int32_t));
 }
 
 }  // namespace
@@ -263,8 +262,7 @@ int32_t pa_varlen_prefill(void* out, const void* q, const void* k_cache, const v
   p.max_context_len = max_context_len;
   p.num_blocks = num_blocks;
   p.scale = scale;
-  p.zero_row = reinterpret_cast<uint4*>(ws + dec_bytes);
-  p.work = reinterpret_cast<int32_t*>(ws + dec_bytes + kAlign);
+  p.work = reinterpret_cast<int32_t*>(ws + dec_bytes);
   p.work_cap =
       prefill_work_capacity(num_seqs, total_q_tokens, num_kv_heads, num_q_heads / num_kv_heads);
   return from_hip(launch_prefill(p, s));

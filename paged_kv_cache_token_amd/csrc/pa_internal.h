@@ -179,7 +179,6 @@ struct PrefillArgs {
   float scale;
   int32_t* work;       // work list in the workspace
   int32_t work_cap;    // capacity in items
-  uint4* zero_row;     // 256 zero bytes in the workspace (source of unusable keys)
 };
 
 hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* cu_seqlens,

@@ -75,7 +75,6 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(PrefillArgs a, int t
   const int t = threadIdx.x;
   const int maxk = max(0, min(a.max_context_len, a.max_blocks_per_seq * kBlockSize));
   for (int i = t; i < kSortBuckets; i += blockDim.x) count[i] = 0;
-  if (t < 16) a.zero_row[t] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
   auto bucket = [&](int s, int q) {
     const int len = a.cu_seqlens[s + 1] - a.cu_seqlens[s];
@@ -141,10 +140,13 @@ __device__ __forceinline__ uint32_t pack_f32_bf16(float lo, float hi) {
 
 #define PA_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-// 16 bytes per lane from global memory straight into LDS: lane i's chunk
-// lands at lds_base + 16 i (lds_base is wave-uniform)
-__device__ __forceinline__ void dma16(const uint4* src, uint4* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, PA_LDS(void, lds_base), 16, 0, 0);
+// 16 bytes per lane from a buffer straight into LDS: lane i's chunk (at
+// byte offset voff of the buffer) lands at lds_base + 16 i (lds_base is
+// wave-uniform); a chunk at or past num_records bytes reads as zeros.
+__device__ __forceinline__ void dma16(const void* base, int num_records, int voff, uint4* lds_base) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, num_records, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, PA_LDS(void, lds_base), 16, voff, 0, 0, 0);
 }
 
 // Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
@@ -166,9 +168,10 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int 
   const int n = lane & 31;             // this lane's query row within the wave
   const int hi = lane >> 5;            // which half of each 16-element k step
 
-  const int lo_row = a.cu_seqlens[seq];
-  const int len = a.cu_seqlens[seq + 1] - lo_row;
-  const int c = a.context_offsets[seq];
+  // per-item metadata, wave-uniform
+  const int lo_row = __builtin_amdgcn_readfirstlane(a.cu_seqlens[seq]);
+  const int len = __builtin_amdgcn_readfirstlane(a.cu_seqlens[seq + 1]) - lo_row;
+  const int c = __builtin_amdgcn_readfirstlane(a.context_offsets[seq]);
   const int q0 = qtile * BMT;
   const int qn = min(BMT, len - q0);   // valid query tokens of this tile (>= 1)
   const int rho = wave * 32 + n;       // row of the item: (head_local, token)
@@ -221,23 +224,31 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int 
   };
   // Loads of tile t into LDS buffer b: wave instruction j = 2*wave + r (of 16
   // per tensor) moves block j/4 of the tile, chunks 4(j%4) .. +3; lane i takes
-  // chunk +i/16 at key position i%16.  Keys past the item's end or in a block
-  // outside the pool read the zero row instead (V must be finite there: p = 0
-  // times a stale NaN would poison the sum; K is masked).
-  const uint4* kc = static_cast<const uint4*>(a.k_cache);
-  const uint4* vc = static_cast<const uint4*>(a.v_cache);
+  // chunk +i/16 at key position i%16.  Each instruction reads one block of
+  // one kv head as a buffer of its valid keys only: keys past the item's end,
+  // and every key of a block outside the pool, arrive as zeros (V must be
+  // finite there: p = 0 times a stale NaN would poison the sum; K is masked).
+  const char* kc = static_cast<const char*>(a.k_cache);
+  const char* vc = static_cast<const char*>(a.v_cache);
+  constexpr int kRowBytes = D * 2;
+  int dma_off[2];  // this lane's byte offset within the block, per instruction
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int ch = 4 * ((2 * wave + r) & 3) + (lane >> 4);
+    dma_off[r] = ((lane & 15) ^ (4 * (ch & 3))) * kRowBytes + ch * 16;
+  }
   auto issue = [&](int t, int b, int e) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int j = 2 * wave + r;
       const int blk = j >> 2, c0 = 4 * (j & 3);
       const int phys = phys_of(e, blk);              // wave-uniform
-      const int ch = c0 + (lane >> 4);
-      const int k16 = (lane & 15) ^ (4 * (ch & 3));
-      const bool ok = phys >= 0 && t * kKeyTile + blk * kBlockSize + k16 < kend;
-      const int64_t row = (((int64_t)max(phys, 0) * hkv + kvh) * kBlockSize + k16) * 16 + ch;
-      dma16(ok ? kc + row : a.zero_row + ch, &sm.k[b][blk][c0][0]);
-      dma16(ok ? vc + row : a.zero_row + ch, &sm.v[b][blk][c0][0]);
+      // (readfirstlane: a buffer descriptor must be scalar)
+      const int nvalid = __builtin_amdgcn_readfirstlane(
+          phys < 0 ? 0 : min(max(kend - (t * kKeyTile + blk * kBlockSize), 0), kBlockSize));
+      const int64_t off = ((int64_t)max(phys, 0) * hkv + kvh) * (kBlockSize * kRowBytes);
+      dma16(kc + off, nvalid * kRowBytes, dma_off[r], &sm.k[b][blk][c0][0]);
+      dma16(vc + off, nvalid * kRowBytes, dma_off[r], &sm.v[b][blk][c0][0]);
     }
   };
 
@@ -271,15 +282,19 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int 
   // l the 4 keys of its dim dt*32 + l%32.
   const int vg = lane >> 4, vs = lane & 15;
   const int vch = 2 * (vg & 1) + ((vs & 3) >> 1);       // chunk within a 32-dim span
+  int v_off[2];  // byte offsets within a V buffer of this lane's two reads at kb = 0, dt = 0
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int k16 = 4 * (vg >> 1) + (vs >> 2) + 8 * h;
+    v_off[h] = vch * 256 + (k16 ^ (4 * vch)) * 16 + 8 * (vs & 1);
+  }
+  const char* v_lds = reinterpret_cast<const char*>(&sm.v[0][0][0][0]);
   auto v_frag = [&](int b, int kb, int dt) -> bf16x8_t {
     uint2 w[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int k16 = 4 * (vg >> 1) + (vs >> 2) + 8 * h;
-      const uint16_t* p = reinterpret_cast<const uint16_t*>(
-          &sm.v[b][kb >> 4][4 * dt + vch][k16 ^ (4 * vch)]);
-      w[h] = lds_read_tr(p + 4 * (vs & 1));
-    }
+    for (int h = 0; h < 2; ++h)
+      w[h] = lds_read_tr(reinterpret_cast<const uint16_t*>(
+          v_lds + v_off[h] + b * (int)sizeof(sm.v[0]) + (kb >> 4) * 4096 + dt * 1024));
     return __builtin_bit_cast(bf16x8_t, make_uint4(w[0].x, w[0].y, w[1].x, w[1].y));
   };
 
@@ -297,8 +312,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int 
     const int bc = t % 3;
     const int bn = bc == 2 ? 0 : bc + 1;
     const int bs = bn == 2 ? 0 : bn + 1;
+    bq |= bad_mask(e2) << 8;  // (read e2 before the tile loads go out)
     if (t + 2 < ntiles) issue(t + 2, bs, e2);
-    bq |= bad_mask(e2) << 8;
     e2 = entries(t + 3);
     const int bad = bq & 15;
     // cur[u][4i+j] is the raw score of key t*64 + 32u + 8i + 4hi + j for this
@@ -429,8 +444,11 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   const int total = a.work[0];
   const int2* items = prefill_items(a.work);
   for (int it = blockIdx.x; it < total; it += gridDim.x) {
+    // the item is wave-uniform: keep it (and all that derives from it) scalar
     const int2 w = items[it];
-    prefill_item<G>(a, w.x, w.y / a.num_kv_heads, w.y % a.num_kv_heads, sm);
+    const int seq = __builtin_amdgcn_readfirstlane(w.x);
+    const int y = __builtin_amdgcn_readfirstlane(w.y);
+    prefill_item<G>(a, seq, y / a.num_kv_heads, y % a.num_kv_heads, sm);
   }
 }
 

@@ -336,13 +336,15 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int 
             cur[u][r] = kNegInf;
         }
     }
-    float mloc = kNegInf;
+    float mm[4] = {kNegInf, kNegInf, kNegInf, kNegInf};  // independent chains
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int r = 0; r < 16; r += 2)
-        mloc = __builtin_elementwise_maximum(mloc,
-                                             __builtin_elementwise_maximum(cur[u][r], cur[u][r + 1]));
+        mm[(r >> 1) & 3] = __builtin_elementwise_maximum(
+            mm[(r >> 1) & 3], __builtin_elementwise_maximum(cur[u][r], cur[u][r + 1]));
+    const float mloc = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mm[0], mm[1]),
+                                                     __builtin_elementwise_maximum(mm[2], mm[3]));
     // the row's other 32 keys sit in lane ^ 32
     const auto mx = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc),
                                                      false, false);
@@ -360,37 +362,53 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int 
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
       m = mn;
     }
-    // the next tile's products (past the last tile they read a stale buffer
-    // and are discarded)
-    scores(bn, nxt);
+    // The next tile's score products (past the last tile they read a stale
+    // buffer and are discarded), interleaved one for one with this tile's
+    // exponentials so the matrix core and the vector ALU work at once; the
+    // K reads run two products ahead.  sched_barrier keeps this order.
     const float moff = -((m == kNegInf) ? 0.f : m) * sl2;
-    float psum = 0.f;
-    uint32_t pf[2][2][4];  // P^T fragments: [half u][16-key step t2][packed pairs]
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};  // partial row sums (independent chains)
+    uint32_t pf[16];  // P^T pairs: pf[8u + 4t2 + e/2] = scores 8t2 + e, +1 of half u
+    auto kread = [&](int i) -> bf16x8_t {
+      const int u = i >> 3, ch = 2 * (i & 7) + hi;
+      return __builtin_bit_cast(bf16x8_t,
+                                sm.k[bn][2 * u + (n >> 4)][ch][(n & 15) ^ (4 * (ch & 3))]);
+    };
+    bf16x8_t kq[3];
+    kq[0] = kread(0);
+    kq[1] = kread(1);
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int i = 0; i < 16; ++i) {
+      if (i + 2 < 16) kq[(i + 2) % 3] = kread(i + 2);
+      const int u = i >> 3, ks = i & 7;
+      if (ks == 0)
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float p0 = fast_exp2(fmaf(cur[u][8 * t2 + e], sl2, moff));
-          const float p1 = fast_exp2(fmaf(cur[u][8 * t2 + e + 1], sl2, moff));
-          psum += p0 + p1;
-          pf[u][t2][e / 2] = pack_f32_bf16(p0, p1);
-        }
-    lsum += psum;
+        for (int r = 0; r < 16; ++r) nxt[u][r] = 0.f;
+      nxt[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[i % 3], qf[ks], nxt[u], 0, 0, 0);
+      const int r = 2 * (i & 7);
+      const float p0 = fast_exp2(fmaf(cur[u][r], sl2, moff));
+      const float p1 = fast_exp2(fmaf(cur[u][r + 1], sl2, moff));
+      ps[i & 3] += p0 + p1;
+      pf[i] = pack_f32_bf16(p0, p1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 
-    // O^T += V^T P^T; k step (u, t2) covers keys 32u + 16t2 + {8(e/4) + 4hi + e%4}
+    // O^T += V^T P^T; k step ut = 2u + t2 covers keys 16ut + {8(e/4) + 4hi + e%4};
+    // the V reads run two products ahead
+    auto vread = [&](int j) -> bf16x8_t { return v_frag(bc, 16 * (j >> 2), j & 3); };
+    bf16x8_t vq[3];
+    vq[0] = vread(0);
+    vq[1] = vread(1);
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const bf16x8_t pb = __builtin_bit_cast(
-            bf16x8_t, make_uint4(pf[u][t2][0], pf[u][t2][1], pf[u][t2][2], pf[u][t2][3]));
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag(bc, 32 * u + 16 * t2, dt), pb,
-                                                          o[dt], 0, 0, 0);
-      }
+    for (int j = 0; j < 16; ++j) {
+      if (j + 2 < 16) vq[(j + 2) % 3] = vread(j + 2);
+      const int ut = j >> 2, dt = j & 3;
+      const bf16x8_t pb = __builtin_bit_cast(
+          bf16x8_t, make_uint4(pf[4 * ut], pf[4 * ut + 1], pf[4 * ut + 2], pf[4 * ut + 3]));
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vq[j % 3], pb, o[dt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     bq >>= 4;
     // this wave's loads of tile t+2 (and the entries of tile t+3) have
     // landed; the barrier publishes them and frees buffer bc

@@ -298,6 +298,14 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int 
     return __builtin_bit_cast(bf16x8_t, make_uint4(w[0].x, w[0].y, w[1].x, w[1].y));
   };
 
+  // Row maxima: mrun is the running maximum of the raw scores seen so far;
+  // m is the reference the exponentials use, p = 2^((s - m) * scale * log2e).
+  // m follows mrun lazily: only when some row's maximum has risen by more
+  // than 2^kLazyRescale over its reference are the accumulators rescaled, so
+  // p stays below 2^kLazyRescale and most tiles skip the 64 products.
+  constexpr float kLazyRescale = 8.f;
+  float mrun = kNegInf;
+
   // One key tile.  Its scores `cur` were computed one step earlier; this
   // step issues the products of tile t+1 into `nxt` (independent of the
   // softmax work on `cur`, so the matrix cores run while the vector ALUs do
@@ -348,19 +356,18 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int 
     // the row's other 32 keys sit in lane ^ 32
     const auto mx = __builtin_amdgcn_permlane32_swap(__float_as_uint(mloc), __float_as_uint(mloc),
                                                      false, false);
-    const float mn = __builtin_elementwise_maximum(
-        m, __builtin_elementwise_maximum(__uint_as_float(mx[0]), __uint_as_float(mx[1])));
-    if (__any(mn != m)) {
-      // some row's max moved: rescale (rows whose max did not move get 1);
-      // kept a real branch so tiles that move no max skip the 64 products
+    mrun = __builtin_elementwise_maximum(
+        mrun, __builtin_elementwise_maximum(__uint_as_float(mx[0]), __uint_as_float(mx[1])));
+    if (__any((mrun - m) * sl2 > kLazyRescale)) {
+      // kept a real branch so tiles that move no reference skip the products
       asm volatile("" ::: "memory");
-      const float alpha = fast_exp2((m - ((mn == kNegInf) ? 0.f : mn)) * sl2);
+      const float alpha = fast_exp2((m - mrun) * sl2);  // 0 while m = -inf
       lsum *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-      m = mn;
+      m = mrun;
     }
     // The next tile's score products (past the last tile they read a stale
     // buffer and are discarded), interleaved one for one with this tile's

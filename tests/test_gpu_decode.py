@@ -158,6 +158,17 @@ def test_gqa_decode_full_sampled(gpu):
     _check_decode(batch, seqs=seqs, check_pools=False)
 
 
+def test_many_pairs_single_partition_sampled(gpu):
+    """>= 4096 (sequence, kv head) pairs with contexts past one 512-token
+    partition: the launch keeps each context in one partition."""
+    rng = np.random.default_rng(28)
+    lens = rng.integers(16, 1500, size=520)
+    batch = W.decode_batch("many_pairs", 28, lens, 32, 8, 128, "bf16")
+    order = np.argsort(batch.context_lens)
+    seqs = sorted(set(order[:3].tolist() + order[-5:].tolist() + list(range(0, 520, 37))))
+    _check_decode(batch, seqs=seqs, check_pools=False)
+
+
 def test_shared_prefix_full_sampled_and_unshared(gpu):
     shared = W.shared_prefix_decode()
     order = np.argsort(shared.context_lens)

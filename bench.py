@@ -286,9 +286,13 @@ def main() -> int:
 
     step_bytes = att_bytes + wr_bytes
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    # the dominant kernel's average duration: with the fused decode step a step
+    # is exactly one launch of it, so timed region 1 gives it without the
+    # per-launch event overhead; otherwise the event pairs of region 2
+    kern_ms = ms_per_step if fused else att_avg_ms
     if kind == "decode" or args.workload == "mixed_step":
         kern_bytes = att_bytes + (wr_bytes if fused else 0)
-        achieved = kern_bytes / (att_avg_ms * 1e-3) / 1e9
+        achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
         traffic = traffic_from_profiles(args.workload, "decode")
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -335,6 +339,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "seq_steps_per_s": round(b.num_seqs / (ms_per_step * 1e-3), 1),
         "attention_call_us": round(att_avg_ms * 1e3, 2),
+        "dominant_kernel_us": round(kern_ms * 1e3, 2),
         "step_calls": "pa_decode_step (fused)" if fused else (
             "pa_build_slot_mapping + pa_write_kv + " +
             ("pa_decode" if kind == "decode" else "pa_varlen_prefill")),

@@ -185,6 +185,67 @@ def traffic_from_profiles(workload: str, kind: str):
 # main
 # --------------------------------------------------------------------------
 
+def context_figures(dbs, run_step, stream, steps, dev) -> dict:
+    """Figures reported beside the measurement, none of them `value`: the
+    warm median (every step on the same layer's caches, so K/V may sit in
+    the 256 MB MALL), a plain device copy's bandwidth, and the step replayed
+    from HIP graphs (one captured step per layer cache; the library makes no
+    allocation, synchronisation or memset, so a captured call is the same
+    launches)."""
+    import torch
+    out = {}
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for s in range(steps):
+        run_step(dbs[0], ev[s])
+    torch.cuda.synchronize()
+    out["warm_call_us_p50"] = round(float(np.median([a.elapsed_time(z) for a, z in ev])) * 1e3, 2)
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    z.record(stream)
+    torch.cuda.synchronize()
+    out["copy_gbs_read_plus_write"] = round(2 * n * reps / (a.elapsed_time(z) * 1e-3) / 1e9, 1)
+    del src, dst
+
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for d in dbs:
+                run_step(d)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for d in dbs:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run_step(d)
+            graphs.append(g)
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        a.record(stream)
+        for s in range(steps):
+            graphs[s % len(graphs)].replay()
+        z.record(stream)
+        torch.cuda.synchronize()
+        out["graph_ms_per_step"] = round(a.elapsed_time(z) / steps, 5)
+        del graphs
+    except Exception as e:  # reported, never fatal: the eager figures stand alone
+        out["graph_ms_per_step"] = None
+        out["graph_error"] = str(e)[:200]
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -201,6 +262,8 @@ def main() -> int:
                     help="decode: three calls (slot mapping, write, decode) instead of one")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the context figures (warm median, copy bandwidth, graph replay)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -284,6 +347,10 @@ def main() -> int:
     att_ms = [a.elapsed_time(z) for a, z in ev]
     att_avg_ms = float(np.mean(att_ms))
 
+    extras = {}
+    if not args.no_extras:
+        extras = context_figures(dbs, run_step, stream, args.steps, dev)
+
     step_bytes = att_bytes + wr_bytes
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     # the dominant kernel's average duration: with the fused decode step a step
@@ -348,7 +415,9 @@ def main() -> int:
         "step_bytes": step_bytes,
         "wall_s_timed": round(wall, 4),
         "kernel_source_hash": kernel_hash(kind),
+        "call_us_p10_p50_p90": [round(float(np.percentile(att_ms, q)) * 1e3, 2) for q in (10, 50, 90)],
     }
+    rec.update(extras)
     if kind == "prefill" or args.workload == "mixed_step":
         fl = prefill_flops(b)
         rec["prefill_flops"] = fl

@@ -16,7 +16,8 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa.so")
-HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "pa.h")
+INCLUDE_DIR = os.path.join(os.path.dirname(_HERE), "include")
+HEADER_PATH = os.path.join(INCLUDE_DIR, "pa.h")
 
 PA_F32, PA_BF16 = 0, 1
 BLOCK_SIZE = 16
@@ -41,6 +42,18 @@ _SIGNATURES = {
     "pa_varlen_prefill": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32,
                                    _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                    _c_i64, _c_f32, _c_i32, _c_p, _c_sz, _c_p]),
+    # host-side block manager (include/pa_blocks.h)
+    "pa_bm_create": (_c_i32, [_c_i64, _c_i32, ctypes.POINTER(_c_p)]),
+    "pa_bm_destroy": (None, [_c_p]),
+    "pa_bm_num_free_blocks": (_c_i64, [_c_p]),
+    "pa_bm_allocate_slots": (_c_i32, [_c_p, _c_i64, _c_i32, _c_i32]),
+    "pa_bm_share_prefix": (_c_i32, [_c_p, _c_i64, _c_i64, _c_i32]),
+    "pa_bm_free_sequence": (_c_i32, [_c_p, _c_i64]),
+    "pa_bm_sequence_info": (_c_i32, [_c_p, _c_i64, ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i32)]),
+    "pa_bm_block_refcount": (_c_i32, [_c_p, _c_i64]),
+    "pa_bm_block_table": (_c_i32, [_c_p, _c_i64, _c_p, _c_i32]),
+    "pa_bm_build_step": (_c_i32, [_c_p, _c_p, _c_p, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                  _c_i64]),
 }
 
 
@@ -75,9 +88,13 @@ def status_string(status: int) -> str:
 
 
 def header_functions() -> list[str]:
-    """Names of the functions include/pa.h declares."""
-    text = open(HEADER_PATH).read()
-    return sorted(set(re.findall(r"^\s*(?:[\w\*]+\s+)+\**(pa_\w+)\s*\(", text, re.M)))
+    """Names of the functions the headers under include/ declare."""
+    names = set()
+    for h in sorted(os.listdir(INCLUDE_DIR)):
+        if h.endswith(".h"):
+            text = open(os.path.join(INCLUDE_DIR, h)).read()
+            names |= set(re.findall(r"^\s*(?:[\w\*]+\s+)+\**(pa_\w+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 # --------------------------------------------------------------------------
@@ -263,6 +280,84 @@ def varlen_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     return out
 
 
-__all__ = ["PAError", "PA_F32", "PA_BF16", "BLOCK_SIZE", "build_slot_mapping", "decode",
+class BlockManager:
+    """Host-side block manager (include/pa_blocks.h): a pool of num_blocks
+    physical blocks, a FIFO free queue, block tables and reference counts,
+    and the builder of a step's attention metadata.  Host-side numpy arrays;
+    copy them to the device for the attention calls."""
+
+    def __init__(self, num_blocks: int, block_size: int = BLOCK_SIZE):
+        h = _c_p()
+        _check("pa_bm_create", lib.pa_bm_create(int(num_blocks), int(block_size), ctypes.byref(h)))
+        self._h = h
+        self._destroy = lib.pa_bm_destroy  # kept: module globals may be gone at exit
+        self.num_blocks = int(num_blocks)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            self._destroy(h)
+            self._h = None
+
+    @property
+    def num_free_blocks(self) -> int:
+        return int(lib.pa_bm_num_free_blocks(self._h))
+
+    def allocate_slots(self, seq_id: int, num_new_tokens: int, num_lookahead_tokens: int = 0) -> bool:
+        """True when the blocks were allocated; False when the free queue is
+        too short (nothing changed)."""
+        st = lib.pa_bm_allocate_slots(self._h, int(seq_id), int(num_new_tokens),
+                                      int(num_lookahead_tokens))
+        if st == 6:  # PA_ERR_NO_FREE_BLOCKS
+            return False
+        _check("pa_bm_allocate_slots", st)
+        return True
+
+    def share_prefix(self, src_seq: int, dst_seq: int, num_tokens: int) -> None:
+        _check("pa_bm_share_prefix", lib.pa_bm_share_prefix(self._h, int(src_seq), int(dst_seq),
+                                                             int(num_tokens)))
+
+    def free(self, seq_id: int) -> None:
+        _check("pa_bm_free_sequence", lib.pa_bm_free_sequence(self._h, int(seq_id)))
+
+    def info(self, seq_id: int) -> tuple[int, int]:
+        """(tokens, blocks) of a sequence."""
+        t, b = _c_i32(), _c_i32()
+        _check("pa_bm_sequence_info", lib.pa_bm_sequence_info(self._h, int(seq_id), ctypes.byref(t),
+                                                               ctypes.byref(b)))
+        return t.value, b.value
+
+    def refcount(self, block_id: int) -> int:
+        return int(lib.pa_bm_block_refcount(self._h, int(block_id)))
+
+    def block_table(self, seq_id: int):
+        import numpy as np
+        _, nb = self.info(seq_id)
+        out = np.empty(max(nb, 1), dtype=np.int32)
+        _check("pa_bm_block_table", lib.pa_bm_block_table(self._h, int(seq_id),
+                                                           out.ctypes.data, out.shape[0]))
+        return out[:nb]
+
+    def build_step(self, seq_ids, q_lens, max_blocks_per_seq: int) -> dict:
+        """Attention metadata of one packed step (host numpy arrays):
+        block_tables, cu_seqlens, context_offsets, context_lens, slot_mapping."""
+        import numpy as np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        ql = np.ascontiguousarray(q_lens, dtype=np.int32)
+        n = ids.shape[0]
+        bt = np.empty((max(n, 1), max_blocks_per_seq), dtype=np.int32)
+        cu = np.empty(n + 1, dtype=np.int32)
+        co = np.empty(max(n, 1), dtype=np.int32)
+        cl = np.empty(max(n, 1), dtype=np.int32)
+        total = int(ql.sum()) if n else 0
+        sm = np.empty(max(total, 1), dtype=np.int64)
+        _check("pa_bm_build_step", lib.pa_bm_build_step(
+            self._h, ids.ctypes.data, ql.ctypes.data, n, int(max_blocks_per_seq), bt.ctypes.data,
+            cu.ctypes.data, co.ctypes.data, cl.ctypes.data, sm.ctypes.data, sm.shape[0]))
+        return {"block_tables": bt[:n], "cu_seqlens": cu, "context_offsets": co[:n],
+                "context_lens": cl[:n], "slot_mapping": sm[:total]}
+
+
+__all__ = ["BlockManager", "PAError", "PA_F32", "PA_BF16", "BLOCK_SIZE", "build_slot_mapping", "decode",
            "decode_step", "decode_workspace_size", "header_functions", "lib", "status_string",
            "varlen_prefill", "varlen_workspace_size", "version", "write_kv"]

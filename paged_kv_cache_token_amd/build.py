@@ -3,8 +3,9 @@
     python paged_kv_cache_token_amd/build.py     (by path: the package itself
                                                  loads libpa.so on import)
 
-compiles every csrc/*.hip file to an object under _build/ (in parallel) and
-links them into paged_kv_cache_token_amd/libpa.so.  It always recompiles.
+compiles every csrc/*.hip file (hipcc, gfx950) and every host-only csrc/*.cpp
+file (g++) to an object under _build/, in parallel, and links them into
+paged_kv_cache_token_amd/libpa.so.  It always recompiles.
 """
 from __future__ import annotations
 
@@ -31,6 +32,16 @@ HIP_FLAGS = [
 ]
 
 
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE]
+
+
+def _cxx() -> str:
+    exe = shutil.which("g++") or shutil.which("c++")
+    if not exe:
+        raise RuntimeError("no host C++ compiler (g++) found")
+    return exe
+
+
 def _hipcc() -> str:
     exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(exe):
@@ -55,10 +66,13 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    objects = [os.path.join(BUILD_DIR, os.path.basename(s) + ".o") for s in sources]
+    host_sources = sorted(glob.glob(os.path.join(CSRC, "*.cpp")))  # host-only C++
+    objects = [os.path.join(BUILD_DIR, os.path.basename(s) + ".o") for s in sources + host_sources]
+    cmds = [[hipcc, *HIP_FLAGS, "-c", s, "-o", o] for s, o in zip(sources, objects)]
+    cmds += [[_cxx(), *CXX_FLAGS, "-c", s, "-o", o]
+             for s, o in zip(host_sources, objects[len(sources):])]
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        futs = [ex.submit(_run, [hipcc, *HIP_FLAGS, "-c", s, "-o", o], verbose)
-                for s, o in zip(sources, objects)]
+        futs = [ex.submit(_run, c, verbose) for c in cmds]
         for f in futs:
             f.result()
     tmp = LIB + ".tmp"

@@ -47,6 +47,7 @@ const char* pa_status_string(int32_t status) {
     case PA_ERR_INVALID_ARGUMENT: return "negative or inconsistent size argument";
     case PA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than the size query returned";
     case PA_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+    case PA_ERR_NO_FREE_BLOCKS: return "not enough free blocks in the pool";
     default: return "unknown status";
   }
 }

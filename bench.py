@@ -246,6 +246,81 @@ def context_figures(dbs, run_step, stream, steps, dev) -> dict:
     return out
 
 
+def bench_block_swap(args, dev) -> int:
+    """pa_swap_blocks on LLaMA-2-7B-shaped pools (4096 blocks of 32 kv heads x
+    16 x 128 bf16, 128 KiB per block per K or V pool): 1024 random blocks of K
+    and of V copied inside device memory (timed: HBM read + write), swapped
+    out to pinned host pools and back in (host-link rates, reported beside)."""
+    import torch
+
+    import paged_kv_cache_token_amd as pa
+    nb, hkv, d, moved = 4096, 32, 128, 1024
+    rng = np.random.default_rng(6)
+    pools = [torch.randn(nb, hkv, 16, d, device=dev).to(torch.bfloat16) for _ in range(2)]
+    ids = rng.permutation(nb)
+    copy_pairs = torch.from_numpy(np.stack([ids[:moved], ids[moved:2 * moved]], 1).astype(np.int64)).to(dev)
+    out_pairs = torch.from_numpy(np.stack([ids[:moved], np.arange(moved)], 1).astype(np.int64)).to(dev)
+    in_pairs = torch.from_numpy(np.stack([np.arange(moved), ids[2 * moved:3 * moved]], 1).astype(np.int64)).to(dev)
+    host = [torch.empty(moved, hkv, 16, d, dtype=torch.bfloat16).pin_memory() for _ in range(2)]
+    block_bytes = hkv * 16 * d * 2
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, steps):
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        torch.cuda.synchronize()
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        z.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(z) / steps
+
+    def copy_step():
+        for p in pools:
+            pa.swap_blocks(p, p, copy_pairs)
+
+    ms = timed(copy_step, args.steps)
+    step_bytes = 2 * 2 * moved * block_bytes  # K and V, read + write
+    value = step_bytes / (ms * 1e-3) / 1e9
+    ms_out = timed(lambda: [pa.swap_blocks(h, p, out_pairs) for h, p in zip(host, pools)], 20)
+    ms_in = timed(lambda: [pa.swap_blocks(p, h, in_pairs) for h, p in zip(host, pools)], 20)
+    link_bytes = 2 * moved * block_bytes
+    cpu = None
+    if not args.no_cpu_baseline:
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        import oracle
+        src = pools[0].cpu().view(torch.int16).numpy()
+        dst = src.copy()
+        pairs = copy_pairs.cpu().numpy()
+        t0, c0, reps = time.perf_counter(), time.process_time(), 0
+        while time.perf_counter() - t0 < min(args.cpu_budget, 5.0):
+            oracle.swap_blocks(dst, src, pairs)
+            reps += 1
+        wall = time.perf_counter() - t0
+        cpu = {"value": round(reps * moved * block_bytes * 2 / wall / 1e9, 3), "unit": "GB/s",
+               "cores": max(1, int(round((time.process_time() - c0) / wall))), "kind": "oracle",
+               "sample": f"oracle block copy of one pool's {moved} pairs, {reps} passes in {wall:.1f} s"}
+    rec = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "block_swap_llama2_pools", "pool_blocks": nb, "kv_heads": hkv,
+                   "head_dim": d, "block_size": 16, "blocks_moved_per_pool": moved,
+                   "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "swap_out_gbs_device_to_pinned_host": round(link_bytes / (ms_out * 1e-3) / 1e9, 2),
+        "swap_in_gbs_pinned_host_to_device": round(link_bytes / (ms_in * 1e-3) / 1e9, 2),
+        "step_calls": "pa_swap_blocks x2 (K and V pools)",
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -253,7 +328,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama2_decode",
                     choices=["llama2_decode", "gqa_decode", "shared_prefix_decode", "mixed_step",
-                             "prefill_chunks", "tiny_decode"])
+                             "prefill_chunks", "tiny_decode", "block_swap"])
     ap.add_argument("--layers", type=int, default=0,
                     help="layer caches to rotate through (0: enough for >= 1 GiB)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -282,6 +357,8 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    if args.workload == "block_swap":
+        return bench_block_swap(args, dev)
     b = make_batch(args.workload)
     kind = "decode" if b.kind == "decode" else "prefill"
     fused = kind == "decode" and not args.unfused

@@ -228,6 +228,34 @@ int32_t pa_varlen_prefill(void* out, const void* q, const void* k_cache, const v
                           int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
                           int32_t dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pa_swap_blocks -- copy whole blocks between two block pools of one layout
+ * ([KW] §2.2: the block manager moves inactive blocks out to host memory
+ * when device memory runs short and back in when they are needed; the same
+ * call copies blocks inside one pool).
+ *
+ *   dst, src         pools of dst_num_blocks / src_num_blocks blocks of
+ *                    block_bytes each (for one K or V cache:
+ *                    num_kv_heads * 16 * head_dim * element bytes).  Each is
+ *                    device memory or pinned host memory (hipHostMalloc,
+ *                    torch pin_memory), which the kernel reads or writes
+ *                    over the host link.
+ *   block_pairs      int64 [num_pairs][2]: (source block, destination block);
+ *                    device or pinned host memory
+ *   block_bytes      a positive multiple of 16
+ *
+ * dst[pair.dst] = src[pair.src], bit for bit.  A pair with an id outside its
+ * pool is skipped.  Two pairs must not write the same destination block, and
+ * within one pool no pair may read a block another pair writes (the order of
+ * the copies is unspecified).
+ * Errors: NULL pointers, num_pairs < 0, block_bytes, a pointer the runtime
+ * knows as neither device nor pinned host memory (PA_ERR_INVALID_ARGUMENT;
+ * nothing is launched).
+ */
+int32_t pa_swap_blocks(void* dst, const void* src, const int64_t* block_pairs, int64_t num_pairs,
+                       int64_t block_bytes, int64_t dst_num_blocks, int64_t src_num_blocks,
+                       void* stream);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

@@ -5,7 +5,7 @@ this package.  It shares no code with the HIP library and imports nothing
 from it.
 """
 from .paged_attention import (BLOCK_SIZE, attend, blocks_needed, decode, gather,
-                              slot_mapping, varlen_prefill, widen, write_kv)
+                              slot_mapping, swap_blocks, varlen_prefill, widen, write_kv)
 
 __all__ = ["BLOCK_SIZE", "attend", "blocks_needed", "decode", "gather",
-           "slot_mapping", "varlen_prefill", "widen", "write_kv"]
+           "slot_mapping", "swap_blocks", "varlen_prefill", "widen", "write_kv"]

@@ -119,6 +119,18 @@ def write_kv(k_cache: np.ndarray, v_cache: np.ndarray, key: np.ndarray,
     v_cache[blk, :, off, :] = value[keep]
 
 
+def swap_blocks(dst: np.ndarray, src: np.ndarray, block_pairs: np.ndarray) -> None:
+    """Copy whole blocks between two pools of one layout, in place: for each
+    (source block, destination block) pair, the destination block becomes a
+    bit copy of the source block ([KW] §2.2: inactive blocks are moved out to
+    host memory and back in when needed).  A pair naming a block outside its
+    pool is skipped.  Pairs are taken one at a time, in order.
+    """
+    for s_blk, d_blk in np.asarray(block_pairs, dtype=np.int64).reshape(-1, 2):
+        if 0 <= s_blk < src.shape[0] and 0 <= d_blk < dst.shape[0]:
+            dst[d_blk] = src[s_blk]
+
+
 def gather(cache: np.ndarray, table_row: np.ndarray, length: int,
            block_size: int = BLOCK_SIZE) -> np.ndarray:
     """One sequence's logically contiguous cache [length, Hkv, d] ([KW] §1.3:

@@ -42,6 +42,7 @@ _SIGNATURES = {
     "pa_varlen_prefill": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32,
                                    _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                    _c_i64, _c_f32, _c_i32, _c_p, _c_sz, _c_p]),
+    "pa_swap_blocks": (_c_i32, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p]),
     # host-side block manager (include/pa_blocks.h)
     "pa_bm_create": (_c_i32, [_c_i64, _c_i32, ctypes.POINTER(_c_p)]),
     "pa_bm_destroy": (None, [_c_p]),
@@ -280,6 +281,39 @@ def varlen_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     return out
 
 
+def _need_pool(t: torch.Tensor, name: str):
+    """A block pool or pair list for pa_swap_blocks: a contiguous device
+    tensor or a contiguous pinned host tensor (the kernel reaches pinned
+    host memory over the host link; pageable memory it cannot)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda" and not (t.device.type == "cpu" and t.is_pinned()):
+        raise ValueError(f"{name} must be a device tensor or a pinned host tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def swap_blocks(dst: torch.Tensor, src: torch.Tensor, block_pairs: torch.Tensor,
+                stream_device: torch.device | None = None) -> None:
+    """dst[pair[1]] = src[pair[0]] for every row of block_pairs (pa_swap_blocks):
+    whole blocks between two pools of one layout ([num_blocks, ...]), each on
+    the device or in pinned host memory.  The copy is enqueued on the current
+    stream of the device tensor among the arguments (or stream_device)."""
+    _need_pool(dst, "dst")
+    _need_pool(src, "src")
+    _need_pool(block_pairs, "block_pairs")
+    if block_pairs.dtype != torch.int64 or block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be int64 [num_pairs, 2]")
+    if dst.dtype != src.dtype or dst.shape[1:] != src.shape[1:]:
+        raise ValueError("dst and src must be pools of one layout")
+    block_bytes = (dst[0].numel() if dst.shape[0] else src[0].numel()) * dst.element_size()
+    dev = stream_device or next((t.device for t in (dst, src, block_pairs) if t.is_cuda),
+                                torch.device("cuda", torch.cuda.current_device()))
+    _check("pa_swap_blocks", lib.pa_swap_blocks(
+        _ptr(dst), _ptr(src), _ptr(block_pairs), block_pairs.shape[0], block_bytes, dst.shape[0],
+        src.shape[0], torch.cuda.current_stream(dev).cuda_stream))
+
+
 class BlockManager:
     """Host-side block manager (include/pa_blocks.h): a pool of num_blocks
     physical blocks, a FIFO free queue, block tables and reference counts,
@@ -358,6 +392,6 @@ class BlockManager:
                 "context_lens": cl[:n], "slot_mapping": sm[:total]}
 
 
-__all__ = ["BlockManager", "PAError", "PA_F32", "PA_BF16", "BLOCK_SIZE", "build_slot_mapping", "decode",
+__all__ = ["BlockManager", "PAError", "swap_blocks", "PA_F32", "PA_BF16", "BLOCK_SIZE", "build_slot_mapping", "decode",
            "decode_step", "decode_workspace_size", "header_functions", "lib", "status_string",
            "varlen_prefill", "varlen_workspace_size", "version", "write_kv"]

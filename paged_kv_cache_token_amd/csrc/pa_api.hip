@@ -80,6 +80,44 @@ int32_t pa_write_kv(const void* key, const void* value, void* k_cache, void* v_c
                                   static_cast<hipStream_t>(stream)));
 }
 
+// The address a kernel uses for p: device memory as is, pinned host memory
+// through its device mapping; nullptr for memory the runtime does not know
+// (pageable host memory would fault the kernel, so it is refused here).
+static void* device_view(const void* p) {
+  hipPointerAttribute_t attr{};
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();  // clear the error the failed query leaves
+    return nullptr;
+  }
+  if (attr.type == hipMemoryTypeDevice) return const_cast<void*>(p);
+  if (attr.type == hipMemoryTypeHost) {
+    void* d = nullptr;
+    if (hipHostGetDevicePointer(&d, const_cast<void*>(p), 0) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    return d;
+  }
+  return nullptr;
+}
+
+int32_t pa_swap_blocks(void* dst, const void* src, const int64_t* block_pairs, int64_t num_pairs,
+                       int64_t block_bytes, int64_t dst_num_blocks, int64_t src_num_blocks,
+                       void* stream) {
+  if (num_pairs < 0 || block_bytes <= 0 || block_bytes % 16 != 0 || dst_num_blocks < 0 ||
+      src_num_blocks < 0)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (num_pairs == 0) return PA_OK;
+  if (!dst || !src || !block_pairs) return PA_ERR_NULL_POINTER;
+  void* d = device_view(dst);
+  void* s = device_view(src);
+  void* pr = device_view(block_pairs);
+  if (!d || !s || !pr) return PA_ERR_INVALID_ARGUMENT;
+  return from_hip(launch_swap_blocks(d, s, static_cast<const int64_t*>(pr), num_pairs, block_bytes,
+                                     dst_num_blocks, src_num_blocks,
+                                     static_cast<hipStream_t>(stream)));
+}
+
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                 int32_t max_context_len, int32_t dtype) {
   if (num_seqs <= 0 || num_q_heads <= 0 || !head_dim_ok(head_dim) || !dtype_ok(dtype)) return 0;

@@ -83,4 +83,37 @@ hipError_t launch_write_kv(const void* key, const void* value, void* k_cache, vo
   return hipGetLastError();
 }
 
+// Whole-block copies between two pools (swap out / in, or inside one pool):
+// one thread per 16-byte piece (grid-stride); consecutive lanes take
+// consecutive pieces of one block, so both sides move contiguous runs.
+__global__ __launch_bounds__(256) void swap_blocks_kernel(uint4* __restrict__ dst,
+                                                          const uint4* __restrict__ src,
+                                                          const int64_t* __restrict__ pairs,
+                                                          int64_t total_pieces, int64_t pieces,
+                                                          int64_t dst_blocks, int64_t src_blocks) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total_pieces;
+       idx += stride) {
+    const int64_t p = idx / pieces;
+    const int64_t piece = idx - p * pieces;
+    const int64_t s = pairs[2 * p], d = pairs[2 * p + 1];
+    if (s < 0 || s >= src_blocks || d < 0 || d >= dst_blocks) continue;
+    dst[d * pieces + piece] = src[s * pieces + piece];
+  }
+}
+
+hipError_t launch_swap_blocks(void* dst, const void* src, const int64_t* pairs, int64_t num_pairs,
+                              int64_t block_bytes, int64_t dst_blocks, int64_t src_blocks,
+                              hipStream_t stream) {
+  const int64_t pieces = block_bytes / 16;
+  const int64_t total = num_pairs * pieces;
+  if (total == 0) return hipSuccess;
+  const int64_t want = (total + 255) / 256;
+  const int gx = (int)std::min<int64_t>(want, 256 * 16);
+  hipLaunchKernelGGL(swap_blocks_kernel, dim3(gx), dim3(256), 0, stream,
+                     static_cast<uint4*>(dst), static_cast<const uint4*>(src), pairs, total, pieces,
+                     dst_blocks, src_blocks);
+  return hipGetLastError();
+}
+
 }  // namespace pa

@@ -108,3 +108,12 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError):
         pa.decode(torch.zeros(1, 1, 64), torch.zeros(1, 1, 16, 64), torch.zeros(1, 1, 16, 64),
                   torch.zeros(1, 1, dtype=torch.int32), torch.ones(1, dtype=torch.int32), 1)
+
+
+def test_swap_blocks_rejects_pageable_host_tensors():
+    """pa_swap_blocks reaches host memory only when it is pinned: the binding
+    refuses plain host tensors before calling the library."""
+    import torch
+    with pytest.raises(ValueError):
+        pa.swap_blocks(torch.zeros(4, 2, 16, 8), torch.zeros(4, 2, 16, 8),
+                       torch.zeros(1, 2, dtype=torch.int64))

@@ -175,6 +175,23 @@ def pin_write_kv_bits():
     assert (kc[0] == 0x7FC1).all() and (np.delete(kc[1, 0], 5, axis=0) == 0x7FC1).all()
 
 
+def pin_swap_blocks_layout():
+    # block b of a pool holds 10*b + 0.5 in every element; pairs move them by
+    # hand-picked ids, one out-of-range pair is skipped, untouched blocks stay
+    src = np.zeros((3, 2, BS, 2))
+    for b in range(3):
+        src[b] = 10 * b + 0.5
+    dst = np.full((4, 2, BS, 2), -1.0)
+    opa.swap_blocks(dst, src, np.array([[2, 0], [0, 3], [1, 9], [7, 1]]))
+    assert (dst[0] == 20.5).all() and (dst[3] == 0.5).all()
+    assert (dst[1] == -1.0).all() and (dst[2] == -1.0).all()
+    # bit copy of bf16 patterns inside one pool (NaN payload, -0)
+    pool = np.zeros((2, 1, BS, 2), np.uint16)
+    pool[0, 0, 3] = [0x7FA5, 0x8000]
+    opa.swap_blocks(pool, pool, np.array([[0, 1]]))
+    assert pool[1, 0, 3].tolist() == [0x7FA5, 0x8000] and (pool[1, 0, :3] == 0).all()
+
+
 def pin_gather_layout():
     # slot value = 100 * physical block + offset, in every head and dim
     cache = np.zeros((3, 2, BS, 2))
@@ -420,6 +437,12 @@ def _mut_write_no_skip(k_cache, v_cache, key, value, slots, block_size=BS):
     v_cache[slots // block_size, :, slots % block_size, :] = value
 
 
+def _mut_swap_reversed(dst, src, block_pairs):
+    for s_blk, d_blk in np.asarray(block_pairs, np.int64).reshape(-1, 2):
+        if 0 <= d_blk < src.shape[0] and 0 <= s_blk < dst.shape[0]:
+            dst[s_blk] = src[d_blk]
+
+
 def _mut_gather_identity(cache, table_row, length, block_size=BS):
     nb = opa.blocks_needed(length, block_size)
     if nb == 0:
@@ -441,6 +464,7 @@ MUTATIONS = {
     "slot_block_offset_swapped": ("slot_mapping", _mut_slot_swap),
     "write_ignores_padding": ("write_kv", _mut_write_no_skip),
     "gather_ignores_table": ("gather", _mut_gather_identity),
+    "swap_pair_reversed": ("swap_blocks", _mut_swap_reversed),
     "gather_transposed": ("gather", _mut_gather_transposed),
     "attend_no_scale": ("attend", _mut_attend("no_scale")),
     "attend_gqa_modulo": ("attend", _mut_attend("gqa_modulo")),

@@ -3,7 +3,7 @@
 // has passed, so a call that returns an error has enqueued nothing.
 
 #include "../../include/pa.h"
-#include "pa_internal.h"
+#include "pa_launch.h"
 
 using namespace pa;
 

@@ -49,7 +49,7 @@
 #include <algorithm>
 
 #include "../../include/pa.h"
-#include "pa_internal.h"
+#include "pa_launch.h"
 
 namespace pa {
 

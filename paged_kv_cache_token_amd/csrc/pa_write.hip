@@ -12,7 +12,7 @@
 
 #include <algorithm>
 
-#include "pa_internal.h"
+#include "pa_launch.h"
 
 namespace pa {
 

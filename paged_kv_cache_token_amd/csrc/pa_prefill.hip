@@ -125,8 +125,8 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(PrefillArgs a, int t
 // of one block); the 16-byte K reads of 16 keys at one chunk, and the
 // transposing 8-byte V reads of 4 keys x 4 chunks, hit distinct banks.
 struct __attribute__((aligned(16))) PrefillShared {
-  uint4 k[3][4][16][16];
-  uint4 v[3][4][16][16];
+  uint4 k[4][4][16][16];
+  uint4 v[4][4][16][16];
 };
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -309,17 +309,27 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int 
   // One key tile.  Its scores `cur` were computed one step earlier; this
   // step issues the products of tile t+1 into `nxt` (independent of the
   // softmax work on `cur`, so the matrix cores run while the vector ALUs do
-  // the exponentials), then O += V^T P^T for tile t.  Three LDS buffers, tile
-  // t in t%3: the loads of tile t+2 go out at the start of step t into the
-  // buffer that held tile t-1, whose last reader finished before the previous
-  // step's barrier, and must land before this step's barrier.  e2 holds the
+  // the exponentials), then O += V^T P^T for tile t.
+  //
+  // The two waves of a SIMD (w and w+4) run the same steps half a step
+  // apart: waves 0-3 meet the step's barrier after the PV products, waves
+  // 4-7 between the score products and the PV products.  So while one does
+  // the exponentials the other feeds the matrix core.  Between barriers t-1
+  // and t, waves 0-3 do softmax(t), scores(t+1) and PV(t); waves 4-7 do
+  // PV(t-1), softmax(t) and scores(t+1).
+  //
+  // Four LDS buffers, tile t in t%4: the loads of tile t+2 go out at the
+  // start of step t into the buffer of tile t-2, whose last readers (PV(t-2):
+  // waves 0-3 before barrier t-2, waves 4-7 before barrier t-1) are done, and
+  // land before barrier t, after which scores(t+2) read them.  e2 holds the
   // table entries of tile t+2; bq the bad-block masks of tiles t, t+1 (and
   // t+2 once added) in 4-bit fields.
+  const bool late = wave >= 4;
   int e2 = 0, bq = 0;
   auto step = [&](int t, f32x16_t(&cur)[2], f32x16_t(&nxt)[2]) {
-    const int bc = t % 3;
-    const int bn = bc == 2 ? 0 : bc + 1;
-    const int bs = bn == 2 ? 0 : bn + 1;
+    const int bc = t & 3;
+    const int bn = (t + 1) & 3;
+    const int bs = (t + 2) & 3;
     bq |= bad_mask(e2) << 8;  // (read e2 before the tile loads go out)
     if (t + 2 < ntiles) issue(t + 2, bs, e2);
     e2 = entries(t + 3);
@@ -400,6 +410,12 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int 
       __builtin_amdgcn_sched_barrier(0);
     }
     lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    if (late) {
+      // this wave's loads of tile t+2 (and the entries of tile t+3) have
+      // landed; the barrier publishes them
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
 
     // O^T += V^T P^T; k step ut = 2u + t2 covers keys 16ut + {8(e/4) + 4hi + e%4};
     // the V reads run two products ahead
@@ -417,10 +433,10 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int 
       __builtin_amdgcn_sched_barrier(0);
     }
     bq >>= 4;
-    // this wave's loads of tile t+2 (and the entries of tile t+3) have
-    // landed; the barrier publishes them and frees buffer bc
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    if (!late) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
   };
 
   if (ntiles > 0) {

@@ -216,9 +216,11 @@ size_t pa_varlen_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32_
  * The K/V of every row (positions up to context_offsets[i] + q_len_i - 1) must
  * already be in the cache (pa_write_kv first).  Row j of sequence i attends
  * keys 0 .. context_offsets[i] + j of its own sequence (causal, its own key
- * included).  Rows of single-token sequences take the decode kernels; longer
- * chunks take the matrix-core prefill kernel.  Element type: PA_BF16; chunks
- * of two or more rows need head_dim 128 (PA_ERR_UNSUPPORTED otherwise).
+ * included).  For PA_BF16 at head_dim 128, rows of single-token sequences
+ * take the decode kernels and longer chunks the matrix-core prefill kernel;
+ * for PA_F32, or head_dim 64, every row takes the decode kernels on its own
+ * (same result, without the matrix-core reuse of each K/V tile across a
+ * chunk's rows).
  */
 int32_t pa_varlen_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* cu_seqlens, const int32_t* context_offsets,

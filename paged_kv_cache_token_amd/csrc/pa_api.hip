@@ -26,6 +26,15 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 size_t varlen_decode_part_bytes(int32_t num_seqs, int32_t hq, int32_t d, int32_t max_ctx) {
   return align_up(decode_ws_bytes(num_seqs, hq, d, decode_max_parts(max_ctx)));
 }
+// Chunks run on the matrix-core kernel for bf16 at head_dim 128; otherwise
+// every packed row goes through the decode kernels as a row of its own.
+bool varlen_matrix_path(int32_t dtype, int32_t head_dim) {
+  return dtype == PA_BF16 && head_dim == 128;
+}
+// row path workspace = [row -> sequence][row -> context][decode partials of every row]
+size_t varlen_rows_bytes(int32_t total_q) {
+  return align_up((size_t)total_q * sizeof(int32_t));
+}
 size_t varlen_work_bytes(int32_t num_seqs, int32_t total_q, int32_t hkv, int32_t group) {
   // count and pad, then two ints per item
   return align_up((size_t)(2 + 2 * (size_t)prefill_work_capacity(num_seqs, total_q, hkv, group)) *
@@ -222,9 +231,12 @@ int32_t pa_decode_step(void* out, const void* q, const void* key, const void* va
 size_t pa_varlen_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32_t num_q_heads,
                                 int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len,
                                 int32_t dtype) {
-  if (num_seqs <= 0 || total_q_tokens < 0 || !head_dim_ok(head_dim) || dtype != PA_BF16 ||
+  if (num_seqs <= 0 || total_q_tokens < 0 || !head_dim_ok(head_dim) || !dtype_ok(dtype) ||
       !heads_ok(num_q_heads, num_kv_heads))
     return 0;
+  if (!varlen_matrix_path(dtype, head_dim))
+    return 2 * varlen_rows_bytes(total_q_tokens) +
+           varlen_decode_part_bytes(total_q_tokens, num_q_heads, head_dim, max_context_len);
   return varlen_decode_part_bytes(num_seqs, num_q_heads, head_dim, max_context_len) +
          varlen_work_bytes(num_seqs, total_q_tokens, num_kv_heads, num_q_heads / num_kv_heads);
 }
@@ -236,13 +248,12 @@ int32_t pa_varlen_prefill(void* out, const void* q, const void* k_cache, const v
                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                           int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
                           int32_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  if (dtype != PA_BF16 || !head_dim_ok(head_dim) || block_size != PA_BLOCK_SIZE ||
+  if (!dtype_ok(dtype) || !head_dim_ok(head_dim) || block_size != PA_BLOCK_SIZE ||
       !heads_ok(num_q_heads, num_kv_heads))
     return PA_ERR_UNSUPPORTED;
   if (num_seqs < 0 || total_q_tokens < 0 || max_q_len < 0 || max_context_len < 0 ||
       max_blocks_per_seq <= 0 || num_blocks <= 0)
     return PA_ERR_INVALID_ARGUMENT;
-  if (max_q_len > 1 && head_dim != 128) return PA_ERR_UNSUPPORTED;  // matrix-core path: d = 128
   if (num_seqs == 0 || total_q_tokens == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !cu_seqlens || !context_offsets || !block_tables)
     return PA_ERR_NULL_POINTER;
@@ -252,6 +263,42 @@ int32_t pa_varlen_prefill(void* out, const void* q, const void* k_cache, const v
   if (!workspace) return PA_ERR_NULL_POINTER;
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
+
+  if (!varlen_matrix_path(dtype, head_dim)) {
+    // every row on its own through the decode kernels: row r of sequence i
+    // attends i's keys 0 .. context_offsets[i] + j
+    int32_t* row_seq = reinterpret_cast<int32_t*>(ws);
+    int32_t* row_ctx = reinterpret_cast<int32_t*>(ws + varlen_rows_bytes(total_q_tokens));
+    hipError_t err = launch_varlen_rows(row_seq, row_ctx, cu_seqlens, context_offsets, num_seqs,
+                                        total_q_tokens, s);
+    if (err != hipSuccess) return PA_ERR_HIP;
+    DecodeArgs r{};
+    r.out = out;
+    r.q = q;
+    r.k_cache = k_cache;
+    r.v_cache = v_cache;
+    r.block_tables = block_tables;
+    r.table_rows = row_seq;
+    r.context_lens = row_ctx;
+    r.num_seqs = total_q_tokens;
+    r.q_rows = total_q_tokens;
+    r.num_q_heads = num_q_heads;
+    r.num_kv_heads = num_kv_heads;
+    r.head_dim = head_dim;
+    r.max_blocks_per_seq = max_blocks_per_seq;
+    r.max_context_len = max_context_len;
+    r.num_blocks = num_blocks;
+    r.scale = scale;
+    r.dtype = dtype;
+    decode_config(total_q_tokens, num_kv_heads, max_context_len, &r.waves, &r.part_tokens,
+                  &r.buffers, &r.grid_mode, &r.oversub);
+    r.max_parts = decode_max_parts(max_context_len, r.part_tokens);
+    if (r.max_parts > 1)
+      r.ws = decode_ws_layout(ws + 2 * varlen_rows_bytes(total_q_tokens), total_q_tokens,
+                              num_q_heads, head_dim, r.max_parts);
+    return from_hip(launch_decode(r, s));
+  }
+
   const size_t dec_bytes =
       varlen_decode_part_bytes(num_seqs, num_q_heads, head_dim, max_context_len);
 

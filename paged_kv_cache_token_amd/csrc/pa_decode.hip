@@ -223,7 +223,9 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int seq, int pa
   // wave's table entries (lane i: the wave's i-th block of the partition; the
   // index is clamped into the table row, so entries past the context are
   // in-bounds garbage that is never used) and the query pieces.
-  const int32_t* table = a.block_tables + (int64_t)seq * a.max_blocks_per_seq + tok0 / kBlockSize;
+  // (rows of a packed call taken one by one name their sequence's table row)
+  const int tseq = a.table_rows ? a.table_rows[seq] : seq;
+  const int32_t* table = a.block_tables + (int64_t)tseq * a.max_blocks_per_seq + tok0 / kBlockSize;
   const int row_left = a.max_blocks_per_seq - tok0 / kBlockSize;  // >= 1 for a live item
   const int my_entry = table[min(wave + nwaves * lane, row_left - 1)];
   int qrow, ctx;
@@ -438,7 +440,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int seq, int pa
   }
 
   if (fused && wave == 0 && lane < LPT) {
-    const int raw = a.block_tables[(int64_t)seq * a.max_blocks_per_seq + (ctx - 1) / kBlockSize];
+    const int raw = a.block_tables[(int64_t)tseq * a.max_blocks_per_seq + (ctx - 1) / kBlockSize];
     if (raw >= 0 && (int64_t)raw < a.num_blocks) {
       const int64_t dst = (((int64_t)raw * hkv + kvh) * kBlockSize + new_off) * LPT + lane;
       static_cast<uint4*>(a.k_cache_w)[dst] = knew;

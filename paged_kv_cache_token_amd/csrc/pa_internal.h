@@ -133,6 +133,8 @@ struct DecodeArgs {
   const void* k_cache;
   const void* v_cache;
   const int32_t* block_tables;
+  const int32_t* table_rows;       // decode mode: block-table row of each query row, or
+                                   // null (row = query row)
   const int32_t* context_lens;     // decode mode: tokens per sequence
   const int32_t* cu_seqlens;       // varlen mode: packed query rows
   const int32_t* context_offsets;  // varlen mode: cached tokens before the row

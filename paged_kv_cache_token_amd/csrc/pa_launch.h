@@ -15,6 +15,10 @@ hipError_t launch_swap_blocks(void* dst, const void* src, const int64_t* pairs, 
                               int64_t block_bytes, int64_t dst_blocks, int64_t src_blocks,
                               hipStream_t stream);
 
+hipError_t launch_varlen_rows(int32_t* row_seq, int32_t* row_ctx, const int32_t* cu_seqlens,
+                              const int32_t* context_offsets, int32_t num_seqs, int32_t q_rows,
+                              hipStream_t stream);
+
 hipError_t launch_write_kv(const void* key, const void* value, void* k_cache, void* v_cache,
                            const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
                            int32_t head_dim, int64_t num_blocks, int32_t elem_bytes,

@@ -83,6 +83,40 @@ hipError_t launch_write_kv(const void* key, const void* value, void* k_cache, vo
   return hipGetLastError();
 }
 
+// Every query row of a packed step as a row of its own: row r of sequence i
+// (its j-th new token, cu_seqlens[i] <= r < cu_seqlens[i+1]) gets table row i
+// and a context of context_offsets[i] + j + 1 keys (causal, its own key
+// included).  One thread per row, a binary search over cu_seqlens; whatever
+// the metadata, the table row stays in [0, num_seqs) and a row no sequence
+// owns gets an empty context.
+__global__ __launch_bounds__(256) void varlen_rows_kernel(
+    int32_t* __restrict__ row_seq, int32_t* __restrict__ row_ctx,
+    const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ context_offsets,
+    int32_t num_seqs, int32_t q_rows) {
+  for (int r = blockIdx.x * blockDim.x + threadIdx.x; r < q_rows; r += gridDim.x * blockDim.x) {
+    int lo = 0, hi = num_seqs;  // first i with cu_seqlens[i + 1] > r
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (cu_seqlens[mid + 1] > r) hi = mid; else lo = mid + 1;
+    }
+    const int i = min(lo, num_seqs - 1);
+    const int start = cu_seqlens[i];
+    const bool owned = lo < num_seqs && start <= r;
+    row_seq[r] = i;
+    row_ctx[r] = owned ? max(0, context_offsets[i] + (r - start) + 1) : 0;
+  }
+}
+
+hipError_t launch_varlen_rows(int32_t* row_seq, int32_t* row_ctx, const int32_t* cu_seqlens,
+                              const int32_t* context_offsets, int32_t num_seqs, int32_t q_rows,
+                              hipStream_t stream) {
+  if (num_seqs == 0 || q_rows == 0) return hipSuccess;
+  const int gx = (int)std::min<int64_t>((q_rows + 255) / 256, 1024);
+  hipLaunchKernelGGL(varlen_rows_kernel, dim3(gx), dim3(256), 0, stream, row_seq, row_ctx,
+                     cu_seqlens, context_offsets, num_seqs, q_rows);
+  return hipGetLastError();
+}
+
 // Whole-block copies between two pools (swap out / in, or inside one pool):
 // one thread per 16-byte piece (grid-stride); consecutive lanes take
 // consecutive pieces of one block, so both sides move contiguous runs.

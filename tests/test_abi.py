@@ -44,7 +44,10 @@ def test_decode_workspace_size():
         4 * 8 * 3 * 130 * 4 + 8 + 4 * 3 * 8
     assert L.pa_decode_workspace_size(4, 8, 96, 513, pa.PA_BF16) == 0        # unsupported d
     assert L.pa_varlen_workspace_size(10, 100, 32, 8, 128, 2000, pa.PA_BF16) > 0
-    assert L.pa_varlen_workspace_size(10, 100, 32, 8, 128, 2000, pa.PA_F32) == 0
+    # fp32 / head_dim 64: every row through the decode kernels, sized per row
+    assert L.pa_varlen_workspace_size(10, 100, 32, 8, 128, 2000, pa.PA_F32) > 0
+    assert L.pa_varlen_workspace_size(10, 100, 32, 8, 64, 2000, pa.PA_BF16) > 0
+    assert L.pa_varlen_workspace_size(10, 100, 32, 8, 96, 2000, pa.PA_BF16) == 0
 
 
 def _decode(**over):
@@ -94,8 +97,9 @@ def test_varlen_host_errors():
     def call(dtype=pa.PA_BF16, d=128, ws=FAKE, wsb=1 << 30, q=FAKE, n=4, total=40, maxq=20):
         return L.pa_varlen_prefill(FAKE, q, FAKE, FAKE, FAKE, FAKE, FAKE, n, total, maxq, 600,
                                    32, 8, d, 16, 64, 1000, 0.1, dtype, ws, wsb, None)
-    assert call(dtype=pa.PA_F32) == 2
+    assert call(dtype=7) == 2
     assert call(d=80) == 2
+    assert call(dtype=pa.PA_F32, q=None) == 1   # fp32 is supported: the pointer check decides
     assert call(q=None) == 1
     assert call(wsb=16) == 4
     assert call(ws=None) == 1

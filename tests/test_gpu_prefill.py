@@ -147,3 +147,28 @@ def test_out_of_pool_block_takes_no_part(gpu, bad_id):
         err = max(err, float(np.abs(got[lo:hi] - want).max()))
     say("max abs err", err)
     assert err <= TOL, err
+
+
+@pytest.mark.parametrize("dtype,d,hq,hkv", [("bf16", 64, 32, 8), ("f32", 128, 8, 8),
+                                            ("f32", 64, 16, 4)])
+def test_varlen_rows_path(gpu, dtype, d, hq, hkv):
+    """fp32 and head_dim 64: every packed row through the decode kernels on its
+    own (causal context per row), decode rows and chunks mixed."""
+    q_lens = [1, 70, 1, 33, 2, 1]
+    ctx = [300, 0, 17, 150, 900, 1]
+    batch = W.varlen_batch(f"rows_{dtype}_{d}_{hq}_{hkv}", 29, q_lens, ctx, hq, hkv, d, dtype)
+    tol = 1e-5 if dtype == "f32" else TOL
+    say(batch.name, "tol", tol)
+    db = _device_batch(batch)
+    out = db.step()
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    hs = host_state(batch)
+    want = expected(batch, hs)
+    err = 0.0
+    for i, rows in want.items():
+        lo, hi = int(batch.cu_seqlens[i]), int(batch.cu_seqlens[i + 1])
+        err = max(err, float(np.abs(got[lo:hi] - rows).max()))
+    say("max abs err", err)
+    assert err <= tol, err

@@ -290,6 +290,7 @@ int32_t pa_varlen_prefill(void* out, const void* q, const void* k_cache, const v
     r.num_blocks = num_blocks;
     r.scale = scale;
     r.dtype = dtype;
+    r.varlen = true;
     decode_config(total_q_tokens, num_kv_heads, max_context_len, &r.waves, &r.part_tokens,
                   &r.buffers, &r.grid_mode, &r.oversub);
     r.max_parts = decode_max_parts(max_context_len, r.part_tokens);

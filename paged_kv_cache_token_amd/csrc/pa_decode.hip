@@ -170,11 +170,19 @@ __device__ __forceinline__ float row_sum4(float x) {
 template <bool VARLEN>
 __device__ __forceinline__ bool decode_row(const DecodeArgs& a, int seq, int& qrow, int& ctx) {
   if constexpr (VARLEN) {
-    const int lo = a.cu_seqlens[seq];
-    if (a.cu_seqlens[seq + 1] - lo != 1) return false;
-    if (lo < 0 || lo >= a.q_rows) return false;  // outside q / out: skipped
-    qrow = lo;
-    ctx = a.context_offsets[seq] + 1;
+    if (a.table_rows) {
+      // every packed row on its own: item `seq` is query row `seq`, with its
+      // own context (its table row comes through table_rows)
+      if (seq >= a.q_rows) return false;
+      qrow = seq;
+      ctx = a.context_lens[seq];
+    } else {
+      const int lo = a.cu_seqlens[seq];
+      if (a.cu_seqlens[seq + 1] - lo != 1) return false;
+      if (lo < 0 || lo >= a.q_rows) return false;  // outside q / out: skipped
+      qrow = lo;
+      ctx = a.context_offsets[seq] + 1;
+    }
   } else {
     qrow = seq;
     ctx = a.context_lens[seq];
@@ -224,7 +232,10 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int seq, int pa
   // index is clamped into the table row, so entries past the context are
   // in-bounds garbage that is never used) and the query pieces.
   // (rows of a packed call taken one by one name their sequence's table row)
-  const int tseq = a.table_rows ? a.table_rows[seq] : seq;
+  int tseq = seq;
+  if constexpr (VARLEN) {
+    if (a.table_rows) tseq = a.table_rows[seq];
+  }
   const int32_t* table = a.block_tables + (int64_t)tseq * a.max_blocks_per_seq + tok0 / kBlockSize;
   const int row_left = a.max_blocks_per_seq - tok0 / kBlockSize;  // >= 1 for a live item
   const int my_entry = table[min(wave + nwaves * lane, row_left - 1)];

@@ -133,9 +133,9 @@ struct DecodeArgs {
   const void* k_cache;
   const void* v_cache;
   const int32_t* block_tables;
-  const int32_t* table_rows;       // decode mode: block-table row of each query row, or
-                                   // null (row = query row)
-  const int32_t* context_lens;     // decode mode: tokens per sequence
+  const int32_t* table_rows;       // varlen mode, rows one by one: block-table row of each
+                                   // packed row (null: single-token sequences only)
+  const int32_t* context_lens;     // decode mode: tokens per sequence; rows one by one: per row
   const int32_t* cu_seqlens;       // varlen mode: packed query rows
   const int32_t* context_offsets;  // varlen mode: cached tokens before the row
   int32_t num_seqs;
@@ -148,7 +148,8 @@ struct DecodeArgs {
   int64_t num_blocks;
   float scale;
   int32_t dtype;                   // PA_F32 / PA_BF16
-  bool varlen;                     // rows come from cu_seqlens; only q_len == 1 seqs
+  bool varlen;                     // rows come from cu_seqlens (only q_len == 1 seqs), or
+                                   // every row on its own through table_rows
   const void* key_new;             // fused step: the new token's K [num_seqs][Hkv][d], or null
   const void* value_new;           // fused step: the new token's V
   void* k_cache_w;                 // fused step: caches to store the new token into

@@ -14,6 +14,9 @@ Sources, cited by page title and section:
         paragraph (the model runner builds a slot mapping and attention
         metadata; all sequences are packed into one super-sequence whose masks
         and positions keep each sequence on its own tokens).
+  [VS]  "vLLMつかったら、ベクトル検索サーバーが高速化して安定性も向上した" --
+        the walk through Scheduler.schedule() (its output carries the number
+        of blocks common to every scheduled request).
   [KW]  "vLLM：颠覆大模型推理的高效API服务引擎深度解析" --
         §1.2 (fixed-size blocks; a per-request block table mapping logical to
         physical blocks with a fill count per block; the 16 / 8 / 0 example),
@@ -198,6 +201,32 @@ def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
         v = widen(gather(v_cache, block_tables[i], n, block_size))
         out[o] = attend(qf[i:i + 1], k, v, np.array([n]), scale)[0]
     return out
+
+
+def cascade_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                   block_tables: np.ndarray, context_lens: np.ndarray,
+                   num_common_prefix_blocks: int, scale: float, seqs=None,
+                   block_size: int = BLOCK_SIZE) -> np.ndarray:
+    """Decode of sequences that share their first ``num_common_prefix_blocks``
+    physical blocks (the scheduler's count of blocks common to every request,
+    [VS] Scheduler.schedule(); blocks referenced read-only by several block
+    tables, [KW] §1.3).
+
+    Attending the common prefix once for all sequences and each private rest
+    on its own, then combining the two by their max-rescaled sums, is the same
+    attention: the result is ``decode`` of the same inputs.  What the split
+    adds is a precondition, checked here: every row's live entries inside the
+    prefix (the first min(P, ceil(len/16)) of them) name the same blocks as
+    row 0's, since the shared pass reads the prefix from row 0 alone.
+    """
+    p = int(num_common_prefix_blocks)
+    if p < 0 or p > block_tables.shape[1]:
+        raise ValueError("num_common_prefix_blocks outside the table")
+    for i in range(len(context_lens)):
+        live = min(p, blocks_needed(int(context_lens[i]), block_size))
+        if not np.array_equal(block_tables[i, :live], block_tables[0, :live]):
+            raise ValueError(f"row {i} does not share the first {live} prefix blocks of row 0")
+    return decode(q, k_cache, v_cache, block_tables, context_lens, scale, seqs, block_size)
 
 
 def varlen_prefill(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,

@@ -192,6 +192,73 @@ def pin_swap_blocks_layout():
     assert pool[1, 0, 3].tolist() == [0x7FA5, 0x8000] and (pool[1, 0, :3] == 0).all()
 
 
+def _cascade_case(seed=11):
+    """Three sequences sharing their first 2 physical blocks (32 tokens) and a
+    fourth whose context (14 tokens) ends inside them; private blocks and a
+    garbage tail after each row's live entries.  Built by hand (no oracle
+    code): pool [10, 2, 16, 4] of float64."""
+    rng = np.random.default_rng(seed)
+    hq, hkv, d = 4, 2, 4
+    kc = rng.standard_normal((10, hkv, BS, d))
+    vc = rng.standard_normal((10, hkv, BS, d))
+    lens = np.array([37, 52, 32, 14])
+    bt = np.array([[6, 2, 9, 0, 5],
+                   [6, 2, 4, 8, 1],
+                   [6, 2, 3, 3, 3],
+                   [6, 7, 7, 7, 7]], np.int32)   # row 3: one live block, so entry 1 is dead
+    q = rng.standard_normal((4, hq, d))
+    return q, kc, vc, bt, lens, hq, hkv, d
+
+
+def pin_cascade_split_identity():
+    # the prefix keys attended on their own and the private rest on their own,
+    # combined with weights e^(m_part - M), by brute-force loops over the
+    # hand-built pool, equal the cascade result
+    q, kc, vc, bt, lens, hq, hkv, d = _cascade_case()
+    scale = 0.5
+    got = opa.cascade_decode(q, kc, vc, bt, lens, 2, scale)
+    g = hq // hkv
+    for i, n in enumerate(lens):
+        keys = [kc[bt[i, t // BS], :, t % BS] for t in range(n)]
+        vals = [vc[bt[i, t // BS], :, t % BS] for t in range(n)]
+        for h in range(hq):
+            parts = []
+            for lo, hi in ((0, min(n, 32)), (32, n)):
+                if hi <= lo:
+                    continue
+                s = [scale * sum(q[i, h, e] * keys[t][h // g][e] for e in range(d))
+                     for t in range(lo, hi)]
+                m = max(s)
+                w = [math.exp(x - m) for x in s]
+                acc = [sum(w[t - lo] * vals[t][h // g][e] for t in range(lo, hi))
+                       for e in range(d)]
+                parts.append((m, sum(w), acc))
+            big = max(p[0] for p in parts)
+            z = sum(math.exp(p[0] - big) * p[1] for p in parts)
+            want = [sum(math.exp(p[0] - big) * p[2][e] for p in parts) / z for e in range(d)]
+            assert np.allclose(got[i, h], want, rtol=0, atol=1e-12), (i, h)
+
+
+def pin_cascade_precondition():
+    q, kc, vc, bt, lens, hq, hkv, d = _cascade_case()
+    # row 3 differs from row 0 only in entry 1, past its one live block: accepted
+    opa.cascade_decode(q, kc, vc, bt, lens, 2, 0.5)
+    bad = bt.copy()
+    bad[1, 1] = 5                                  # a live prefix entry differs
+
+    def rejected(table, p):
+        try:
+            opa.cascade_decode(q, kc, vc, table, lens, p, 0.5)
+        except ValueError:
+            return True
+        return False
+    assert rejected(bad, 2)
+    assert rejected(bt, 6)                         # more blocks than the table holds
+    # no common prefix: the plain decode
+    assert np.array_equal(opa.cascade_decode(q, kc, vc, bad, lens, 0, 0.5),
+                          opa.decode(q, kc, vc, bad, lens, 0.5))
+
+
 def pin_gather_layout():
     # slot value = 100 * physical block + offset, in every head and dim
     cache = np.zeros((3, 2, BS, 2))
@@ -443,6 +510,30 @@ def _mut_swap_reversed(dst, src, block_pairs):
             dst[s_blk] = src[d_blk]
 
 
+def _mut_cascade_checks_dead_entries(q, k_cache, v_cache, block_tables, context_lens,
+                                     num_common_prefix_blocks, scale, seqs=None, block_size=BS):
+    p = int(num_common_prefix_blocks)
+    if (np.asarray(block_tables)[:, :p] != np.asarray(block_tables)[0, :p]).any():
+        raise ValueError("prefix differs")
+    return opa.decode(q, k_cache, v_cache, block_tables, context_lens, scale, seqs, block_size)
+
+
+def _mut_cascade_prefix_twice(q, k_cache, v_cache, block_tables, context_lens,
+                              num_common_prefix_blocks, scale, seqs=None, block_size=BS):
+    # the shared keys counted once more in every row that holds them
+    qf = opa.widen(q)
+    p = int(num_common_prefix_blocks) * block_size
+    out = np.zeros(qf.shape)
+    for i, n in enumerate(context_lens):
+        n = int(n)
+        k = opa.widen(opa.gather(k_cache, block_tables[i], n, block_size))
+        v = opa.widen(opa.gather(v_cache, block_tables[i], n, block_size))
+        kk = np.concatenate([k[:min(n, p)], k])
+        vv = np.concatenate([v[:min(n, p)], v])
+        out[i] = opa.attend(qf[i:i + 1], kk, vv, np.array([len(kk)]), scale)[0]
+    return out
+
+
 def _mut_gather_identity(cache, table_row, length, block_size=BS):
     nb = opa.blocks_needed(length, block_size)
     if nb == 0:
@@ -465,6 +556,8 @@ MUTATIONS = {
     "write_ignores_padding": ("write_kv", _mut_write_no_skip),
     "gather_ignores_table": ("gather", _mut_gather_identity),
     "swap_pair_reversed": ("swap_blocks", _mut_swap_reversed),
+    "cascade_checks_dead_entries": ("cascade_decode", _mut_cascade_checks_dead_entries),
+    "cascade_prefix_twice": ("cascade_decode", _mut_cascade_prefix_twice),
     "gather_transposed": ("gather", _mut_gather_transposed),
     "attend_no_scale": ("attend", _mut_attend("no_scale")),
     "attend_gqa_modulo": ("attend", _mut_attend("gqa_modulo")),

@@ -84,6 +84,23 @@ class DeviceBatch:
         self.write_new()
         return self.attend()
 
+    def cascade(self, out: torch.Tensor | None = None,
+                prefix_blocks: int | None = None) -> torch.Tensor:
+        """Decode attention through pa_cascade_decode, the common prefix being
+        the batch's shared prompt (or ``prefix_blocks`` blocks)."""
+        b = self.b
+        assert b.kind == "decode"
+        if prefix_blocks is None:
+            prefix_blocks = b.notes["prefix_tokens"] // b.block_size
+        size = pa.cascade_workspace_size(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim,
+                                         b.max_context_len, prefix_blocks, b.torch_dtype)
+        if getattr(self, "cascade_ws", None) is None or self.cascade_ws.numel() < size:
+            self.cascade_ws = torch.empty(max(size, 1), dtype=torch.uint8, device=self.device)
+        out = self.out if out is None else out
+        return pa.cascade_decode(self.q, self.k_cache, self.v_cache, self.block_tables,
+                                 self.context_lens, b.max_context_len, prefix_blocks, b.scale,
+                                 out=out, workspace=self.cascade_ws)
+
     def fused_step(self, out: torch.Tensor | None = None) -> torch.Tensor:
         """The same decode step in one launch (pa_decode_step)."""
         b = self.b

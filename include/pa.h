@@ -190,6 +190,47 @@ int32_t pa_decode_step(void* out, const void* q, const void* key, const void* va
                        void* stream);
 
 /*
+ * Bytes of device workspace pa_cascade_decode needs for these shapes (never
+ * less than pa_decode_workspace_size of the same shapes).  Depends on shapes
+ * only.
+ */
+size_t pa_cascade_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len,
+                                 int32_t num_common_prefix_blocks, int32_t dtype);
+
+/*
+ * pa_cascade_decode -- pa_decode for sequences whose block tables begin with
+ * the same physical blocks: a common prompt prefix whose blocks every table
+ * references read-only ([KW] §1.3: blocks shared by several block tables;
+ * "vLLMつかったら、ベクトル検索サーバーが高速化して安定性も向上した", the walk
+ * through Scheduler.schedule(): a step's scheduler output carries the number
+ * of blocks common to all of its requests).
+ *
+ *   num_common_prefix_blocks  P, in [0, max_blocks_per_seq]: the first P
+ *                         entries of every block-table row name the same
+ *                         blocks (precondition; only row 0's are read for
+ *                         them).  A sequence whose context ends inside the
+ *                         prefix attends only its first context_lens[i] keys.
+ *   workspace             device scratch of >= pa_cascade_workspace_size(...)
+ *                         bytes
+ *   other arguments  as pa_decode
+ *
+ * The same attention as pa_decode (up to rounding order and the bf16 rounding
+ * of the prefix's softmax weights).  For bf16 at head_dim 128 the prefix is
+ * attended once per kv head for all sequences on the matrix cores, its rows
+ * being the g query heads of each sequence, and the rest of every context by
+ * the decode kernels; the partial results are combined by their
+ * max-rescaled sums.  Other types and head sizes, and P = 0, run pa_decode.
+ */
+int32_t pa_cascade_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                          int32_t max_context_len, int64_t num_blocks,
+                          int32_t num_common_prefix_blocks, float scale, int32_t dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device workspace pa_varlen_prefill needs for these shapes.
  */
 size_t pa_varlen_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32_t num_q_heads,

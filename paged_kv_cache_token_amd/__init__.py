@@ -38,6 +38,10 @@ _SIGNATURES = {
     "pa_decode_step": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32,
                                 _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_f32, _c_i32,
                                 _c_p, _c_sz, _c_p]),
+    "pa_cascade_workspace_size": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "pa_cascade_decode": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
+                                   _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_f32, _c_i32,
+                                   _c_p, _c_sz, _c_p]),
     "pa_varlen_workspace_size": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "pa_varlen_prefill": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32,
                                    _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
@@ -240,6 +244,44 @@ def decode_step(q: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
         _ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
         _ptr(block_tables), _ptr(context_lens), n, hq, hkv, d, bs, block_tables.shape[1],
         int(max_context_len), num_blocks, scale, _DTYPES[q.dtype], _ptr(workspace), ws_bytes,
+        _stream(q)))
+    return out
+
+
+def cascade_workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                           max_context_len: int, num_common_prefix_blocks: int,
+                           dtype: torch.dtype) -> int:
+    return int(lib.pa_cascade_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                             max_context_len, num_common_prefix_blocks,
+                                             _DTYPES[dtype]))
+
+
+def cascade_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                   num_common_prefix_blocks: int, scale: float | None = None,
+                   out: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode of sequences whose tables share their first blocks
+    (pa_cascade_decode); returns out [num_seqs, Hq, d]."""
+    for t, nm in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, nm)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    num_blocks, hkv, bs, d = _cache_dims(k_cache)
+    n, hq, dq = q.shape
+    if dq != d or q.dtype not in _DTYPES or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q / cache head_dim or dtype mismatch")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype)
+    scale = float(d ** -0.5 if scale is None else scale)
+    size = cascade_workspace_size(n, hq, hkv, d, max_context_len, num_common_prefix_blocks,
+                                  q.dtype)
+    workspace, ws_bytes = _workspace(size, q, workspace)
+    _check("pa_cascade_decode", lib.pa_cascade_decode(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        n, hq, hkv, d, bs, block_tables.shape[1], int(max_context_len), num_blocks,
+        int(num_common_prefix_blocks), scale, _DTYPES[q.dtype], _ptr(workspace), ws_bytes,
         _stream(q)))
     return out
 

@@ -2,6 +2,10 @@
 // dispatch to the kernels.  Nothing here touches the GPU before every check
 // has passed, so a call that returns an error has enqueued nothing.
 
+#include <stdlib.h>
+
+#include <algorithm>
+
 #include "../../include/pa.h"
 #include "pa_launch.h"
 
@@ -39,6 +43,34 @@ size_t varlen_work_bytes(int32_t num_seqs, int32_t total_q, int32_t hkv, int32_t
   // count and pad, then two ints per item
   return align_up((size_t)(2 + 2 * (size_t)prefill_work_capacity(num_seqs, total_q, hkv, group)) *
                   sizeof(int32_t));
+}
+
+// The common-prefix pass runs on the matrix-core kernel: bf16 at head_dim 128.
+bool cascade_matrix_path(int32_t dtype, int32_t head_dim) {
+  return dtype == PA_BF16 && head_dim == 128;
+}
+constexpr int kCascadeKeyTile = 64;  // keys per tile of the matrix-core kernel
+// Tiles per prefix item: enough items to give every compute unit one (256
+// items) but at least two tiles each, so the per-item start-up (query and
+// first tiles in flight) is paid over several tiles.  Shapes only.
+int cascade_split_tiles(int num_seqs, int num_kv_heads, int group, int prefix_tokens) {
+  const int tiles = ceil_div(prefix_tokens, kCascadeKeyTile);
+  const int pairs = ceil_div(num_seqs, prefill_tile_tokens(group)) * num_kv_heads;
+  int st = std::max(2, (int)(((int64_t)tiles * pairs + 255) / 256));
+  const char* e = getenv("PA_CASCADE_SPLIT_TILES");  // tuning override (>= 1)
+  if (e && *e) {
+    const int v = atoi(e);
+    if (v >= 1) st = v;
+  }
+  return std::min(st, std::max(tiles, 1));
+}
+// Partial slots per (seq, q head): the prefix splits (at most one per tile),
+// then the partitions of the rest of the longest context.
+int cascade_max_parts(int32_t max_context_len, int32_t prefix_blocks, int part_tokens,
+                      int splits) {
+  const int prefix_tokens = prefix_blocks * PA_BLOCK_SIZE;
+  if (splits <= 0) splits = std::max(1, ceil_div(prefix_tokens, kCascadeKeyTile));
+  return splits + decode_max_parts(std::max(max_context_len - prefix_tokens, 0), part_tokens);
 }
 
 }  // namespace
@@ -226,6 +258,102 @@ int32_t pa_decode_step(void* out, const void* q, const void* key, const void* va
   if (a.max_parts > 1)
     a.ws = decode_ws_layout(workspace, num_seqs, num_q_heads, head_dim, a.max_parts);
   return from_hip(launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t pa_cascade_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len,
+                                 int32_t num_common_prefix_blocks, int32_t dtype) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || !head_dim_ok(head_dim) || !dtype_ok(dtype) ||
+      num_common_prefix_blocks < 0)
+    return 0;
+  const size_t plain =
+      pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, dtype);
+  if (num_common_prefix_blocks == 0 || !cascade_matrix_path(dtype, head_dim)) return plain;
+  const size_t split = decode_ws_bytes(num_seqs, num_q_heads, head_dim,
+                                       cascade_max_parts(max_context_len, num_common_prefix_blocks,
+                                                         kMinPartitionTokens, 0));
+  return split > plain ? split : plain;
+}
+
+int32_t pa_cascade_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                          int32_t max_context_len, int64_t num_blocks,
+                          int32_t num_common_prefix_blocks, float scale, int32_t dtype,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(head_dim) || block_size != PA_BLOCK_SIZE ||
+      !heads_ok(num_q_heads, num_kv_heads))
+    return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || num_blocks <= 0 ||
+      num_common_prefix_blocks < 0 || num_common_prefix_blocks > max_blocks_per_seq)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return PA_ERR_NULL_POINTER;
+  const size_t need = pa_cascade_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                max_context_len, num_common_prefix_blocks, dtype);
+  if (workspace_bytes < need) return PA_ERR_WORKSPACE_TOO_SMALL;
+  if (need > 0 && !workspace) return PA_ERR_NULL_POINTER;
+  if (num_common_prefix_blocks == 0 || !cascade_matrix_path(dtype, head_dim))
+    return pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, block_size, max_blocks_per_seq, max_context_len,
+                     num_blocks, scale, dtype, workspace, workspace_bytes, stream);
+
+  const int group = num_q_heads / num_kv_heads;
+  const int prefix_tokens = num_common_prefix_blocks * PA_BLOCK_SIZE;
+  const int split_tiles = cascade_split_tiles(num_seqs, num_kv_heads, group, prefix_tokens);
+  const int splits = ceil_div(ceil_div(prefix_tokens, kCascadeKeyTile), split_tiles);
+
+  DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.q_rows = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.num_blocks = num_blocks;
+  a.scale = scale;
+  a.dtype = dtype;
+  a.varlen = false;
+  decode_config(num_seqs, num_kv_heads, max_context_len, &a.waves, &a.part_tokens, &a.buffers,
+                &a.grid_mode, &a.oversub);
+  a.key_start = prefix_tokens;
+  a.prefix_parts = splits;
+  a.max_parts = cascade_max_parts(max_context_len, num_common_prefix_blocks, a.part_tokens, splits);
+  a.ws = decode_ws_layout(workspace, num_seqs, num_q_heads, head_dim, a.max_parts);
+
+  PrefillArgs p{};
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.num_seqs = num_seqs;
+  p.total_q_tokens = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.max_context_len = max_context_len;
+  p.num_blocks = num_blocks;
+  p.scale = scale;
+  p.part_ml = a.ws.ml;
+  p.part_acc = a.ws.acc;
+  p.max_parts = a.max_parts;
+  p.prefix_tokens = prefix_tokens;
+  p.split_tiles = split_tiles;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t err = launch_cascade_prefix(p, splits, st);
+  if (err != hipSuccess) return from_hip(err);
+  return from_hip(launch_decode(a, st));
 }
 
 size_t pa_varlen_workspace_size(int32_t num_seqs, int32_t total_q_tokens, int32_t num_q_heads,

@@ -191,8 +191,9 @@ __device__ __forceinline__ bool decode_row(const DecodeArgs& a, int seq, int& qr
   return true;
 }
 
-__device__ __forceinline__ int parts_of(int ctx, int part_tokens) {
-  return max(1, ceil_div(ctx, part_tokens));
+// partitions of `keys` keys (one, possibly empty, when keys <= 0)
+__device__ __forceinline__ int parts_of(int keys, int part_tokens) {
+  return max(1, ceil_div(keys, part_tokens));
 }
 
 template <int G, int D>
@@ -225,7 +226,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int seq, int pa
   const int hq = a.num_q_heads;
   const int hkv = a.num_kv_heads;
   const int pt = a.part_tokens;
-  const int tok0 = part * pt;
+  const int tok0 = a.key_start + part * pt;
 
   // Three independent loads go out together: the context length (scalar), this
   // wave's table entries (lane i: the wave's i-th block of the partition; the
@@ -241,7 +242,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int seq, int pa
   const int my_entry = table[min(wave + nwaves * lane, row_left - 1)];
   int qrow, ctx;
   if (!decode_row<VARLEN>(a, seq, qrow, ctx)) return;
-  const int nparts = parts_of(ctx, pt);
+  const int nparts = parts_of(ctx - a.key_start, pt);
   if (part >= nparts) return;
   uint4 qv[G];
   // the new token's K/V (fused step) travel with the query pieces
@@ -518,11 +519,11 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int seq, int pa
       lsum += wt * sm.ml[w][h][1];
       asum += wt * sm.acc[w][h][d];
     }
-    if (nparts == 1) {
+    if (nparts == 1 && a.prefix_parts == 0) {
       store_elem<BF16>(a.out, ((int64_t)qrow * hq + kvh * G + h) * D + d,
                        lsum > 0.f ? asum / lsum : 0.f);
     } else {
-      const int64_t pidx = (row_base + h) * a.max_parts + part;
+      const int64_t pidx = (row_base + h) * a.max_parts + a.prefix_parts + part;
       a.ws.acc[pidx * D + d] = asum;
       if (d == 0) {
         a.ws.ml[pidx * 2 + 0] = mx;
@@ -542,7 +543,7 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
   const int seq = blockIdx.y;
   int qrow, ctx;
   if (!decode_row<VARLEN>(a, seq, qrow, ctx)) return;
-  const int nparts = parts_of(ctx, a.part_tokens);
+  const int nparts = a.prefix_parts + parts_of(ctx - a.key_start, a.part_tokens);
   if (nparts <= 1) return;
   const int hq = a.num_q_heads;
   const int d = threadIdx.x;
@@ -605,6 +606,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a) {
   for (int s = s0; s < s1; ++s) {
     int qrow, ctx;
     if (!decode_row<VARLEN>(a, s, qrow, ctx)) continue;
+    ctx = max(ctx - a.key_start, 0);  // keys this call attends
     full += ctx / pt;
     partial += (ctx % pt != 0 || ctx == 0) ? 1 : 0;
   }
@@ -625,6 +627,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(DecodeArgs a) {
   for (int s = s0; s < s1; ++s) {
     int qrow, ctx;
     if (!decode_row<VARLEN>(a, s, qrow, ctx)) continue;
+    ctx = max(ctx - a.key_start, 0);
     const int nf = ctx / pt;
     for (int p = 0; p < nf; ++p) a.ws.items[pos_full++] = make_int2(s, p);
     if (ctx % pt != 0 || ctx == 0) a.ws.items[pos_part++] = make_int2(s, nf);

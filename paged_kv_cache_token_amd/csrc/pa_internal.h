@@ -161,6 +161,11 @@ struct DecodeArgs {
   int32_t buffers;                 // K/V register buffers per wave (2..4)
   int32_t grid_mode;               // multi-partition: 1 = (seq, kvh, part) grid, 0 = work list
   int32_t oversub;                 // persistent grid = oversub x resident workgroups
+  int32_t key_start;               // keys [0, key_start) of every context are attended
+                                   // elsewhere (a common prefix); partitions start there
+  int32_t prefix_parts;            // partial slots [0, prefix_parts) of every (seq, q head)
+                                   // hold that prefix's partials; this call's partitions
+                                   // follow them, and the merge takes all of them
 };
 
 struct PrefillArgs {
@@ -182,6 +187,14 @@ struct PrefillArgs {
   float scale;
   int32_t* work;       // work list in the workspace
   int32_t work_cap;    // capacity in items
+  // common-prefix pass of a decode call (the rows are the sequences' single
+  // query rows; the keys are the first prefix_tokens of block-table row 0)
+  const int32_t* context_lens;
+  float* part_ml;      // decode partial slots: (max in log2 units, sum) ...
+  float* part_acc;     // ... and unnormalised accumulators, max_parts per (seq, q head)
+  int32_t max_parts;
+  int32_t prefix_tokens;
+  int32_t split_tiles; // 64-key tiles per item; item x of a row tile fills partial slot x
 };
 
 }  // namespace pa

@@ -156,7 +156,13 @@ __device__ __forceinline__ uint2 lds_read_tr(const uint16_t* p) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(PA_LDS(i16x4_t, p)));
 }
 
-template <int G>
+// One work item.  Prefill (CASCADE = false): sequence `seq`, query tile
+// `qtile`, kv head `kvh`; rows are (q head, token) of the tile.  Common-prefix
+// pass (CASCADE = true): `seq` is the key split (tiles split*split_tiles ..),
+// the rows are (q head, sequence) for sequences qtile*256/G ..; every row
+// sees the prefix keys below its own context length, and the item writes
+// unnormalised partials instead of the output.
+template <int G, bool CASCADE>
 __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int qtile, int kvh,
                                              PrefillShared& sm) {
   constexpr int D = kPrefillD;
@@ -169,9 +175,17 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int 
   const int hi = lane >> 5;            // which half of each 16-element k step
 
   // per-item metadata, wave-uniform
-  const int lo_row = __builtin_amdgcn_readfirstlane(a.cu_seqlens[seq]);
-  const int len = __builtin_amdgcn_readfirstlane(a.cu_seqlens[seq + 1]) - lo_row;
-  const int c = __builtin_amdgcn_readfirstlane(a.context_offsets[seq]);
+  int lo_row, len, c;
+  if constexpr (CASCADE) {
+    lo_row = 0;
+    len = a.num_seqs;
+    c = 0;
+  } else {
+    lo_row = __builtin_amdgcn_readfirstlane(a.cu_seqlens[seq]);
+    len = __builtin_amdgcn_readfirstlane(a.cu_seqlens[seq + 1]) - lo_row;
+    c = __builtin_amdgcn_readfirstlane(a.context_offsets[seq]);
+  }
+  const int tile0 = CASCADE ? seq * a.split_tiles : 0;  // first key tile of the item
   const int q0 = qtile * BMT;
   const int qn = min(BMT, len - q0);   // valid query tokens of this tile (>= 1)
   const int rho = wave * 32 + n;       // row of the item: (head_local, token)
@@ -180,15 +194,29 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int 
   // rows outside the packed q / out arrays (inconsistent metadata) are skipped
   const bool valid_q =
       tok < qn && lo_row >= 0 && (int64_t)lo_row + q0 + tok < (int64_t)a.total_q_tokens;
-  const int qpos = c + q0 + tok;       // absolute position of this row
-  // keys any row of the item sees, clamped to the declared maxima
-  const int kend = max(0, min(c + q0 + qn, min(a.max_context_len, a.max_blocks_per_seq * kBlockSize)));
-  const int row_lim = valid_q ? min(qpos + 1, kend) : 0;  // keys [0, row_lim) are visible
-  const int full_lim = min(c + q0 + 1, kend);  // keys every row of the item sees
-  const int ntiles = ceil_div(kend, kKeyTile);
+  const int kmax = min(a.max_context_len, a.max_blocks_per_seq * kBlockSize);
+  int kend, row_lim, full_lim;
+  if constexpr (CASCADE) {
+    // keys of the split; a row sees those below its context length
+    kend = max(0, min(min((tile0 + a.split_tiles) * kKeyTile, a.prefix_tokens), kmax));
+    const int ctx = valid_q ? max(0, min(a.context_lens[q0 + tok], kmax)) : 0;
+    row_lim = min(ctx, kend);
+    // keys every valid row of this wave sees (masking is decided per wave)
+    int lim = valid_q ? row_lim : 0x7fffffff;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) lim = min(lim, __shfl_xor(lim, off));
+    full_lim = __builtin_amdgcn_readfirstlane(lim);
+  } else {
+    const int qpos = c + q0 + tok;       // absolute position of this row
+    // keys any row of the item sees, clamped to the declared maxima
+    kend = max(0, min(c + q0 + qn, kmax));
+    row_lim = valid_q ? min(qpos + 1, kend) : 0;  // keys [0, row_lim) are visible
+    full_lim = min(c + q0 + 1, kend);  // keys every row of the item sees
+  }
+  const int ntiles = max(0, ceil_div(kend, kKeyTile) - tile0);
   const int hkv = a.num_kv_heads;
   const int hq = a.num_q_heads;
-  const int32_t* table = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
+  const int32_t* table = a.block_tables + (CASCADE ? 0 : (int64_t)seq * a.max_blocks_per_seq);
 
   // B operand of S^T = K Q^T: this lane's query row, dims ks*16 + hi*8 .. +8
   bf16x8_t qf[8];
@@ -209,7 +237,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int 
   // the in-flight tile loads.  Entries past the table's end are clamped (their
   // keys lie past the item's end).
   auto entries = [&](int t) -> int {
-    return table[min(t * 4 + (lane & 3), a.max_blocks_per_seq - 1)];
+    return table[min((tile0 + t) * 4 + (lane & 3), a.max_blocks_per_seq - 1)];
   };
   auto phys_of = [&](int e, int blk) -> int {
     const int phys = __builtin_amdgcn_readlane(e, blk);
@@ -245,7 +273,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int 
       const int phys = phys_of(e, blk);              // wave-uniform
       // (readfirstlane: a buffer descriptor must be scalar)
       const int nvalid = __builtin_amdgcn_readfirstlane(
-          phys < 0 ? 0 : min(max(kend - (t * kKeyTile + blk * kBlockSize), 0), kBlockSize));
+          phys < 0 ? 0 : min(max(kend - ((tile0 + t) * kKeyTile + blk * kBlockSize), 0), kBlockSize));
       const int64_t off = ((int64_t)max(phys, 0) * hkv + kvh) * (kBlockSize * kRowBytes);
       dma16(kc + off, nvalid * kRowBytes, dma_off[r], &sm.k[b][blk][c0][0]);
       dma16(vc + off, nvalid * kRowBytes, dma_off[r], &sm.v[b][blk][c0][0]);
@@ -337,7 +365,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int 
     // cur[u][4i+j] is the raw score of key t*64 + 32u + 8i + 4hi + j for this
     // row; the running max m is kept in raw units (scale > 0) and the scale
     // is folded into the exponent: p = 2^(s*scale*log2e - m*scale*log2e)
-    const int kt0 = t * kKeyTile;
+    const int kt0 = (tile0 + t) * kKeyTile;
     // every key of the tile visible to every row: no masking
     const bool full = bad == 0 && kt0 + kKeyTile <= full_lim;
     if (!full) {
@@ -371,7 +399,9 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int 
     if (__any((mrun - m) * sl2 > kLazyRescale)) {
       // kept a real branch so tiles that move no reference skip the products
       asm volatile("" ::: "memory");
-      const float alpha = fast_exp2((m - mrun) * sl2);  // 0 while m = -inf
+      // 0 while m = -inf; 1 for a row that has seen no key yet (all of its
+      // keys so far masked: nothing accumulated, and -inf - -inf is NaN)
+      const float alpha = fast_exp2(mrun == kNegInf ? 0.f : (m - mrun) * sl2);
       lsum *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
@@ -462,6 +492,26 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int 
   const auto ls = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum),
                                                    false, false);
   const float ltot = __uint_as_float(ls[0]) + __uint_as_float(ls[1]);
+  if constexpr (CASCADE) {
+    // partial slot `seq` (the split) of (sequence q0 + tok, head): the
+    // reference the exponentials used, in log2 units, the sum and the
+    // unnormalised accumulators
+    if (valid_q) {
+      const int64_t pidx = ((int64_t)(q0 + tok) * hq + head) * a.max_parts + seq;
+      float* acc = a.part_acc + pidx * D;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<float4*>(acc + dt * 32 + 8 * i + 4 * hi) =
+              make_float4(o[dt][4 * i], o[dt][4 * i + 1], o[dt][4 * i + 2], o[dt][4 * i + 3]);
+      if (hi == 0) {
+        a.part_ml[pidx * 2] = m == kNegInf ? kNegInf : m * sl2;
+        a.part_ml[pidx * 2 + 1] = ltot;
+      }
+    }
+    return;
+  }
   if (valid_q) {
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     uint16_t* out = static_cast<uint16_t*>(a.out) + ((int64_t)(lo_row + q0 + tok) * hq + head) * D;
@@ -489,8 +539,15 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
     const int2 w = items[it];
     const int seq = __builtin_amdgcn_readfirstlane(w.x);
     const int y = __builtin_amdgcn_readfirstlane(w.y);
-    prefill_item<G>(a, seq, y / a.num_kv_heads, y % a.num_kv_heads, sm);
+    prefill_item<G, false>(a, seq, y / a.num_kv_heads, y % a.num_kv_heads, sm);
   }
+}
+
+// Common-prefix pass: item (split, row tile, kv head) = (x, y, z).
+template <int G>
+__global__ __launch_bounds__(kPrefillThreads) void cascade_prefix_kernel(PrefillArgs a) {
+  __shared__ PrefillShared sm;
+  prefill_item<G, true>(a, blockIdx.x, blockIdx.y, blockIdx.z, sm);
 }
 
 static int prefill_cus() {
@@ -521,6 +578,24 @@ static hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t stream) {
   const int gx = (int)std::max<int64_t>(1, std::min<int64_t>(a.work_cap, want));
   hipLaunchKernelGGL((prefill_kernel<G>), dim3(gx), dim3(kPrefillThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int G>
+static hipError_t launch_cascade_g(const PrefillArgs& a, int splits, hipStream_t stream) {
+  const dim3 grid(splits, ceil_div(a.num_seqs, prefill_tile_tokens(G)), a.num_kv_heads);
+  hipLaunchKernelGGL((cascade_prefix_kernel<G>), grid, dim3(kPrefillThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_cascade_prefix(const PrefillArgs& a, int splits, hipStream_t stream) {
+  if (a.head_dim != kPrefillD || splits <= 0) return hipErrorInvalidValue;
+  switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: return launch_cascade_g<1>(a, splits, stream);
+    case 2: return launch_cascade_g<2>(a, splits, stream);
+    case 4: return launch_cascade_g<4>(a, splits, stream);
+    case 8: return launch_cascade_g<8>(a, splits, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {

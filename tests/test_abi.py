@@ -107,6 +107,37 @@ def test_varlen_host_errors():
     assert call(n=0, q=None) == 0
 
 
+def test_cascade_workspace_size():
+    ws = L.pa_cascade_workspace_size
+    dec = L.pa_decode_workspace_size
+    # no common prefix, or a type without the matrix-core pass: pa_decode's size
+    assert ws(4, 8, 2, 128, 513, 0, pa.PA_BF16) == dec(4, 8, 128, 513, pa.PA_BF16)
+    assert ws(4, 8, 2, 128, 513, 8, pa.PA_F32) == dec(4, 8, 128, 513, pa.PA_F32)
+    assert ws(4, 8, 2, 64, 513, 8, pa.PA_BF16) == dec(4, 8, 64, 513, pa.PA_BF16)
+    # 8 prefix blocks = 128 keys = at most 2 prefix splits, then the rest of
+    # a 300-token context in one 256-token partition: 3 slots of (m, l, acc[128])
+    # per (seq, q head), the item count and the (seq, partition) list
+    assert ws(4, 8, 2, 128, 300, 8, pa.PA_BF16) == 4 * 8 * 3 * 130 * 4 + 8 + 4 * 3 * 8
+    # a context that fits one partition still needs partial slots
+    assert dec(4, 8, 128, 200, pa.PA_BF16) == 0 and ws(4, 8, 2, 128, 200, 4, pa.PA_BF16) > 0
+    assert ws(4, 8, 2, 128, 300, -1, pa.PA_BF16) == 0
+
+
+def test_cascade_host_errors():
+    def call(p=4, dtype=pa.PA_BF16, d=128, q=FAKE, n=4, ws=FAKE, wsb=1 << 30, maxb=8):
+        return L.pa_cascade_decode(FAKE, q, FAKE, FAKE, FAKE, FAKE, n, 8, 2, d, 16, maxb, 300,
+                                   64, p, 0.1, dtype, ws, wsb, None)
+    assert call(dtype=7) == 2
+    assert call(d=96) == 2
+    assert call(p=-1) == 3
+    assert call(p=9) == 3          # more common blocks than a table row holds
+    assert call(n=-1) == 3
+    assert call(q=None) == 1
+    assert call(wsb=16) == 4
+    assert call(ws=None) == 1
+    assert call(n=0, q=None) == 0
+
+
 def test_binding_rejects_host_tensors():
     import torch
     with pytest.raises(ValueError):

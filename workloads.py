@@ -355,10 +355,12 @@ def prefill_only(seed: int = 4, n_prefill: int = 8) -> PagedBatch:
 
 
 def shared_prefix_decode(seed: int = 5, n: int = 128, prefix_blocks: int = 64,
-                         suffix_range=(16, 31744), unshared: bool = False) -> PagedBatch:
+                         suffix_range=(16, 31744), unshared: bool = False,
+                         num_q_heads: int = 32, num_kv_heads: int = 8, head_dim: int = 128,
+                         dtype: str = "bf16") -> PagedBatch:
     """n decode sequences whose tables all start with the same prefix_blocks
     physical blocks (a 1024-token shared prompt), then private suffixes of
-    U[16, 31744] tokens; 32 q / 8 kv heads, d=128, bf16.
+    U[16, 31744] tokens; 32 q / 8 kv heads, d=128, bf16 (the defaults).
 
     With ``unshared=True`` the same token values are laid out with a private
     copy of the prefix per sequence (the comparison case: outputs must match).
@@ -399,8 +401,11 @@ def shared_prefix_decode(seed: int = 5, n: int = 128, prefix_blocks: int = 64,
         flen = np.stack([np.full(n, prefix_tokens), priv_len], axis=1).reshape(-1)
         fsrc = np.stack([np.zeros(n, np.int64), priv_src], axis=1).reshape(-1).astype(np.int32)
     fcu = np.concatenate([[0], np.cumsum(flen)]).astype(np.int32)
-    b = PagedBatch(name="shared_prefix_decode_bf16" + ("_unshared" if unshared else ""),
-                   dtype="bf16", num_q_heads=32, num_kv_heads=8, head_dim=128,
+    shape = "" if (num_q_heads, num_kv_heads, head_dim) == (32, 8, 128) else \
+        f"_{num_q_heads}_{num_kv_heads}_{head_dim}"
+    b = PagedBatch(name=f"shared_prefix_decode_{dtype}{shape}" + ("_unshared" if unshared else ""),
+                   dtype=dtype, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                   head_dim=head_dim,
                    num_blocks=pool, block_tables=bt, cu_seqlens=cu, context_offsets=c_off,
                    fill_seq=fseq, fill_start=fstart, fill_cu=fcu, seed=seed, kind="decode",
                    fill_src=fsrc, num_values=num_values,

@@ -45,6 +45,9 @@ KERNEL_SOURCES = {
                "paged_kv_cache_token_amd/csrc/pa_internal.h"],
     "prefill": ["paged_kv_cache_token_amd/csrc/pa_prefill.hip",
                 "paged_kv_cache_token_amd/csrc/pa_internal.h"],
+    "cascade": ["paged_kv_cache_token_amd/csrc/pa_decode.hip",
+                "paged_kv_cache_token_amd/csrc/pa_prefill.hip",
+                "paged_kv_cache_token_amd/csrc/pa_internal.h"],
 }
 
 
@@ -61,6 +64,9 @@ def make_batch(name: str):
         "llama2_decode": W.llama2_decode,
         "gqa_decode": W.gqa_decode,
         "shared_prefix_decode": W.shared_prefix_decode,
+        "shared_prefix_cascade": W.shared_prefix_decode,
+        "long_prefix_decode": W.long_prefix_decode,
+        "long_prefix_cascade": W.long_prefix_decode,
         "mixed_step": W.mixed_step,
         "prefill_chunks": W.prefill_only,
         "tiny_decode": W.tiny_decode,
@@ -327,8 +333,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama2_decode",
-                    choices=["llama2_decode", "gqa_decode", "shared_prefix_decode", "mixed_step",
-                             "prefill_chunks", "tiny_decode", "block_swap"])
+                    choices=["llama2_decode", "gqa_decode", "shared_prefix_decode",
+                             "shared_prefix_cascade", "long_prefix_decode",
+                             "long_prefix_cascade", "mixed_step", "prefill_chunks",
+                             "tiny_decode", "block_swap"])
     ap.add_argument("--layers", type=int, default=0,
                     help="layer caches to rotate through (0: enough for >= 1 GiB)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -361,7 +369,9 @@ def main() -> int:
         return bench_block_swap(args, dev)
     b = make_batch(args.workload)
     kind = "decode" if b.kind == "decode" else "prefill"
-    fused = kind == "decode" and not args.unfused
+    # the shared-prefix batch through pa_cascade_decode (new tokens stored first)
+    cascade = args.workload.endswith("_cascade")
+    fused = kind == "decode" and not args.unfused and not cascade
     att_bytes = attention_bytes(b)
     # the fused step reads the new K/V rows and stores them: no slot array traffic
     wr_bytes = fused_write_bytes(b) if fused else write_bytes(b)
@@ -390,7 +400,10 @@ def main() -> int:
         d.write_new()
         if ev_pair:
             ev_pair[0].record(stream)
-        d.attend()
+        if cascade:
+            d.cascade()
+        else:
+            d.attend()
         if ev_pair:
             ev_pair[1].record(stream)
 
@@ -486,12 +499,13 @@ def main() -> int:
         "dominant_kernel_us": round(kern_ms * 1e3, 2),
         "step_calls": "pa_decode_step (fused)" if fused else (
             "pa_build_slot_mapping + pa_write_kv + " +
-            ("pa_decode" if kind == "decode" else "pa_varlen_prefill")),
+            ("pa_cascade_decode" if cascade else
+             "pa_decode" if kind == "decode" else "pa_varlen_prefill")),
         "attention_bytes": att_bytes,
         "write_bytes": wr_bytes,
         "step_bytes": step_bytes,
         "wall_s_timed": round(wall, 4),
-        "kernel_source_hash": kernel_hash(kind),
+        "kernel_source_hash": kernel_hash("cascade" if cascade else kind),
         "call_us_p10_p50_p90": [round(float(np.percentile(att_ms, q)) * 1e3, 2) for q in (10, 50, 90)],
     }
     rec.update(extras)

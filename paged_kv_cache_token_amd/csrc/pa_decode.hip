@@ -550,14 +550,37 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
   const int64_t prow = ((int64_t)seq * hq + h) * a.max_parts;
   const float* ml = a.ws.ml + prow * 2;
   const float* pacc = a.ws.acc + prow * D + d;
+  // partials are read U at a time, all loads of a batch issued before any
+  // is used (indices past the last partition are clamped, their values
+  // unused), so the latency is paid once per batch instead of per partition
+  constexpr int U = 8;
   float mx = kNegInf;
-  for (int p = 0; p < nparts; ++p) mx = fmaxf(mx, ml[2 * p]);
+  for (int p = 0; p < nparts; p += U) {
+    float mv[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) mv[j] = ml[2 * min(p + j, nparts - 1)];
+#pragma unroll
+    for (int j = 0; j < U; ++j) mx = fmaxf(mx, mv[j]);
+  }
   const float mref = (mx == kNegInf) ? 0.f : mx;
   float lsum = 0.f, asum = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    const float wt = fast_exp2(ml[2 * p] - mref);
-    lsum += wt * ml[2 * p + 1];
-    asum += wt * pacc[(int64_t)p * D];
+  for (int p = 0; p < nparts; p += U) {
+    float mv[U], lv[U], av[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int q = min(p + j, nparts - 1);
+      mv[j] = ml[2 * q];
+      lv[j] = ml[2 * q + 1];
+      av[j] = pacc[(int64_t)q * D];
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      if (p + j < nparts) {
+        const float wt = fast_exp2(mv[j] - mref);
+        lsum += wt * lv[j];
+        asum += wt * av[j];
+      }
+    }
   }
   store_elem<BF16>(a.out, ((int64_t)qrow * hq + h) * D + d, lsum > 0.f ? asum / lsum : 0.f);
 }

@@ -413,6 +413,16 @@ def shared_prefix_decode(seed: int = 5, n: int = 128, prefix_blocks: int = 64,
     return b
 
 
+def long_prefix_decode(seed: int = 6, n: int = 128) -> PagedBatch:
+    """A long common prompt and short private parts: n = 128 decode sequences
+    whose tables start with the same 256 blocks (4096 tokens), then private
+    suffixes of U[16, 1024] tokens; 32 q / 8 kv heads, d=128, bf16.  The case
+    a common-prefix split is for: the prefix is ~85% of every context."""
+    b = shared_prefix_decode(seed=seed, n=n, prefix_blocks=256, suffix_range=(16, 1024))
+    b.name = "long_prefix_decode_bf16"
+    return b
+
+
 CONFIGS = {
     "tiny_decode": tiny_decode,
     "llama2_decode": llama2_decode,

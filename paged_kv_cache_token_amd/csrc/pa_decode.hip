@@ -600,14 +600,126 @@ __global__ __launch_bounds__(256) void decode_grid_kernel(DecodeArgs a) {
   decode_item<BF16, D, G, VARLEN, NB>(a, blockIdx.x, blockIdx.z, blockIdx.y, sm);
 }
 
+// The work list without a plan launch: each workgroup derives, from the
+// lengths, the same (sequence, partition) order the plan kernel writes (every
+// full-length partition in sequence order, then each sequence's shorter last
+// one) as two exclusive scans in LDS: ex_full[s], the full partitions before
+// sequence s, and ex_part[s], the short ones.  Item i < total_full belongs to
+// the last s with ex_full[s] <= i; the rest likewise in ex_part.
+constexpr int kInlinePlanChunk = 8;  // sequences per thread (up to 2048 with 4 waves)
+
+template <bool VARLEN>
+__device__ __forceinline__ void inline_plan(const DecodeArgs& a, int* ex_full, int* ex_part,
+                                            int& total_full, int& total) {
+  __shared__ int wtot[2][kDecodeMaxWaves];
+  const int n = a.num_seqs;
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int nw = blockDim.x >> 6;
+  const int chunk = ceil_div(n, (int)blockDim.x);  // <= kInlinePlanChunk
+  const int s0 = min(n, t * chunk);
+  int nf[kInlinePlanChunk], np[kInlinePlanChunk];
+  int full = 0, part = 0;
+#pragma unroll
+  for (int j = 0; j < kInlinePlanChunk; ++j) {
+    nf[j] = 0;
+    np[j] = 0;
+    const int s = s0 + j;
+    int qrow, ctx;
+    if (j < chunk && s < n && decode_row<VARLEN>(a, s, qrow, ctx)) {
+      ctx = max(ctx - a.key_start, 0);
+      nf[j] = ctx / a.part_tokens;
+      np[j] = (ctx % a.part_tokens != 0 || ctx == 0) ? 1 : 0;
+    }
+    full += nf[j];
+    part += np[j];
+  }
+  // inclusive scans over the wave, then over the waves' totals
+  int fi = full, pi = part;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int fu = __shfl_up(fi, off), pu = __shfl_up(pi, off);
+    if (lane >= off) {
+      fi += fu;
+      pi += pu;
+    }
+  }
+  if (lane == 63) {
+    wtot[0][wave] = fi;
+    wtot[1][wave] = pi;
+  }
+  __syncthreads();
+  int fbase = 0, pbase = 0;
+  total_full = 0;
+  int total_part = 0;
+  for (int w = 0; w < nw; ++w) {
+    if (w < wave) {
+      fbase += wtot[0][w];
+      pbase += wtot[1][w];
+    }
+    total_full += wtot[0][w];
+    total_part += wtot[1][w];
+  }
+  total = total_full + total_part;
+  int fx = fbase + fi - full, px = pbase + pi - part;  // exclusive, at s0
+#pragma unroll
+  for (int j = 0; j < kInlinePlanChunk; ++j) {
+    const int s = s0 + j;
+    if (j < chunk && s < n) {
+      ex_full[s] = fx;
+      ex_part[s] = px;
+    }
+    fx += nf[j];
+    px += np[j];
+  }
+  __syncthreads();
+}
+
+// last s in [0, n) with ex[s] <= x (ex non-decreasing, ex[0] = 0 <= x): a
+// 64-way search, each lane testing one candidate per round
+__device__ __forceinline__ int plan_find(const int* ex, int n, int x) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, hi = n;
+  while (hi - lo > 1) {
+    const int step = ceil_div(hi - lo, 64);
+    const int cand = lo + lane * step;
+    const bool ok = cand < hi && ex[cand] <= x;
+    const unsigned long long b = __ballot(ok);  // bit 0 is set: ex[lo] <= x
+    lo += (63 - __builtin_clzll(b)) * step;
+    hi = min(hi, lo + step);
+  }
+  return lo;
+}
+
 // Persistent workgroups walk the (sequence, partition) list for kv head blockIdx.y.
 template <bool BF16, int D, int G, bool VARLEN, int NB>
 __global__ __launch_bounds__(256) void decode_list_kernel(DecodeArgs a) {
   __shared__ DecodeShared<G, D> sm;
-  const int total = *a.ws.count;
+  extern __shared__ int plan_lds[];  // inline plan: ex_full[n], ex_part[n]
+  int total, total_full = 0;
+  if (a.inline_plan)
+    inline_plan<VARLEN>(a, plan_lds, plan_lds + a.num_seqs, total_full, total);
+  else
+    total = *a.ws.count;
   for (int it = blockIdx.x; it < total; it += gridDim.x) {
-    const int2 w = a.ws.items[it];
-    decode_item<BF16, D, G, VARLEN, NB>(a, w.x, w.y, blockIdx.y, sm);
+    int seq, part;
+    if (a.inline_plan) {
+      const int* ex_full = plan_lds;
+      if (it < total_full) {
+        seq = plan_find(ex_full, a.num_seqs, it);
+        part = it - ex_full[seq];
+      } else {
+        seq = plan_find(plan_lds + a.num_seqs, a.num_seqs, it - total_full);
+        part = (seq + 1 < a.num_seqs ? ex_full[seq + 1] : total_full) - ex_full[seq];
+      }
+      seq = __builtin_amdgcn_readfirstlane(seq);
+      part = __builtin_amdgcn_readfirstlane(part);
+    } else {
+      const int2 w = a.ws.items[it];
+      seq = w.x;
+      part = w.y;
+    }
+    decode_item<BF16, D, G, VARLEN, NB>(a, seq, part, blockIdx.y, sm);
   }
 }
 
@@ -685,9 +797,14 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
                        dim3(D), 0, stream, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((decode_plan_kernel<VARLEN>), dim3(1), dim3(1024), 0, stream, a);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  size_t plan_lds = 0;
+  if (a.inline_plan) {
+    plan_lds = 2 * sizeof(int) * (size_t)a.num_seqs;
+  } else {
+    hipLaunchKernelGGL((decode_plan_kernel<VARLEN>), dim3(1), dim3(1024), 0, stream, a);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   static int per_cu[kDecodeMaxWaves + 1] = {0, 0, 0, 0, 0};
   if (per_cu[a.waves] == 0) {
     int nb = 0;
@@ -704,7 +821,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   const int gx = (int)std::max<int64_t>(
       1, std::min<int64_t>(items_bound, (want + a.num_kv_heads - 1) / a.num_kv_heads));
   hipLaunchKernelGGL((decode_list_kernel<BF16, D, G, VARLEN, NB>), dim3(gx, a.num_kv_heads), block,
-                     0, stream, a);
+                     plan_lds, stream, a);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((decode_merge_kernel<BF16, D, VARLEN>), dim3(a.num_q_heads, a.num_seqs),
@@ -789,8 +906,15 @@ void decode_config(int num_seqs, int num_kv_heads, int max_context_len, int* wav
   *oversub = (eo >= 1 && eo <= 8) ? eo : 4;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-  if (a.num_seqs == 0) return hipSuccess;
+bool decode_inline_plan(int num_seqs, int waves) {
+  // every thread of the workgroup scans at most kInlinePlanChunk sequences
+  return num_seqs <= kInlinePlanChunk * 64 * waves && env_int("PA_DECODE_INLINE_PLAN", 1) != 0;
+}
+
+hipError_t launch_decode(const DecodeArgs& args, hipStream_t stream) {
+  if (args.num_seqs == 0) return hipSuccess;
+  DecodeArgs a = args;
+  a.inline_plan = decode_inline_plan(a.num_seqs, a.waves) ? 1 : 0;
   return a.dtype == PA_BF16 ? launch_dim<true>(a, stream) : launch_dim<false>(a, stream);
 }
 

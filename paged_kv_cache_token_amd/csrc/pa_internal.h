@@ -163,6 +163,8 @@ struct DecodeArgs {
   int32_t oversub;                 // persistent grid = oversub x resident workgroups
   int32_t key_start;               // keys [0, key_start) of every context are attended
                                    // elsewhere (a common prefix); partitions start there
+  int32_t inline_plan;             // work list mode: each workgroup derives the item list
+                                   // itself (no plan kernel); needs num_seqs <= 2048
   int32_t prefix_parts;            // partial slots [0, prefix_parts) of every (seq, q head)
                                    // hold that prefix's partials; this call's partitions
                                    // follow them, and the merge takes all of them

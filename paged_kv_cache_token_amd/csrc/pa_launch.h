@@ -28,6 +28,8 @@ hipError_t launch_write_kv(const void* key, const void* value, void* k_cache, vo
 // (so a call's result never depends on where its blocks live).
 void decode_config(int num_seqs, int num_kv_heads, int max_context_len, int* waves,
                    int* part_tokens, int* buffers, int* grid_mode, int* oversub);
+// whether a work-list launch derives its list in every workgroup (no plan kernel)
+bool decode_inline_plan(int num_seqs, int waves);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 // rows per prefill work item and bound on the number of items

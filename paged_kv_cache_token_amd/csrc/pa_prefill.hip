@@ -71,47 +71,72 @@ __device__ __forceinline__ int2* prefill_items(int32_t* work) {
 // its own rows.
 __global__ __launch_bounds__(1024) void prefill_plan_kernel(PrefillArgs a, int tile_tokens) {
   __shared__ int count[kSortBuckets];
+  __shared__ int wave_tot[1024 / 64];
   const int n = a.num_seqs;
   const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
   const int maxk = max(0, min(a.max_context_len, a.max_blocks_per_seq * kBlockSize));
   for (int i = t; i < kSortBuckets; i += blockDim.x) count[i] = 0;
+  // this thread's first sequence, read once (the common case: n <= 1024)
+  int len0 = 0, c0 = 0;
+  if (t < n) {
+    const int lo = a.cu_seqlens[t];
+    len0 = a.cu_seqlens[t + 1] - lo;
+    c0 = a.context_offsets[t];
+  }
   __syncthreads();
-  auto bucket = [&](int s, int q) {
-    const int len = a.cu_seqlens[s + 1] - a.cu_seqlens[s];
+  auto seq_meta = [&](int s, int& len, int& c) {
+    if (s == t) {
+      len = len0;
+      c = c0;
+    } else {
+      len = a.cu_seqlens[s + 1] - a.cu_seqlens[s];
+      c = a.context_offsets[s];
+    }
+  };
+  auto bucket = [&](int len, int c, int q) {
     const int qn = min(tile_tokens, len - q * tile_tokens);
-    const int kend = max(0, min(a.context_offsets[s] + q * tile_tokens + qn, maxk));
+    const int kend = max(0, min(c + q * tile_tokens + qn, maxk));
     return min(ceil_div(kend, kKeyTile), kSortBuckets - 1);
   };
   for (int s = t; s < n; s += blockDim.x) {
-    const int len = a.cu_seqlens[s + 1] - a.cu_seqlens[s];
+    int len, c;
+    seq_meta(s, len, c);
     if (len < 2) continue;
     const int nt = ceil_div(len, tile_tokens);
-    for (int q = 0; q < nt; ++q) atomicAdd(&count[bucket(s, q)], a.num_kv_heads);
+    for (int q = 0; q < nt; ++q) atomicAdd(&count[bucket(len, c, q)], a.num_kv_heads);
   }
   __syncthreads();
-  // exclusive offsets, largest bucket first: thread t owns bucket 1023 - t and
-  // the counts are scanned over t
+  // exclusive offsets, largest bucket first: thread t owns bucket 1023 - t;
+  // inclusive scans inside each wave, then over the waves' totals
   static_assert(kSortBuckets == 1024, "one bucket per thread");
-  __shared__ int scan[kSortBuckets];
   const int mine = count[kSortBuckets - 1 - t];
-  scan[t] = mine;
-  __syncthreads();
-  for (int off = 1; off < kSortBuckets; off <<= 1) {
-    const int add = t >= off ? scan[t - off] : 0;
-    __syncthreads();
-    scan[t] += add;
-    __syncthreads();
+  int inc = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int up = __shfl_up(inc, off);
+    if (lane >= off) inc += up;
   }
-  count[kSortBuckets - 1 - t] = scan[t] - mine;
-  if (t == kSortBuckets - 1) a.work[0] = min(scan[t], a.work_cap);
+  if (lane == 63) wave_tot[wave] = inc;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < 1024 / 64; ++w) {
+    const int v = wave_tot[w];
+    base += w < wave ? v : 0;
+    total += v;
+  }
+  count[kSortBuckets - 1 - t] = base + inc - mine;
+  if (t == 0) a.work[0] = min(total, a.work_cap);
   __syncthreads();
   int2* items = prefill_items(a.work);
   for (int s = t; s < n; s += blockDim.x) {
-    const int len = a.cu_seqlens[s + 1] - a.cu_seqlens[s];
+    int len, c;
+    seq_meta(s, len, c);
     if (len < 2) continue;
     const int nt = ceil_div(len, tile_tokens);
     for (int q = 0; q < nt; ++q) {
-      const int pos = atomicAdd(&count[bucket(s, q)], a.num_kv_heads);
+      const int pos = atomicAdd(&count[bucket(len, c, q)], a.num_kv_heads);
       for (int h = 0; h < a.num_kv_heads; ++h)
         if (pos + h < a.work_cap) items[pos + h] = make_int2(s, q * a.num_kv_heads + h);
     }

@@ -247,3 +247,41 @@ def test_decode_out_of_pool_block_takes_no_part(gpu, bad_id):
     err = _max_err(got, want)
     say("max abs err", err)
     assert err <= TOL["bf16"], err
+
+
+# ---- work list derived in every workgroup vs the plan kernel ------------------
+
+@pytest.mark.parametrize("name", ["gqa", "ragged_g8", "varlen_mixed", "varlen_rows_f32"])
+def test_inline_plan_equals_plan_kernel(gpu, monkeypatch, name):
+    """The list kernel's own work list (the default) and the plan kernel's
+    list name the same (sequence, partition) items: bit-identical outputs."""
+    lens = [1, 2, 15, 16, 17, 100, 511, 512, 513, 1024, 1100, 2049, 0]
+    batch = {
+        "gqa": W.gqa_decode,
+        "ragged_g8": lambda: W.decode_batch("il_g8", 33, lens[:-1], 16, 2, 128, "bf16",
+                                            pool_factor=1.3),
+        "varlen_mixed": lambda: W.varlen_batch("il_vm", 34, [1, 1, 300, 1, 64, 1],
+                                               [700, 1500, 200, 20, 900, 2500], 32, 8, 128,
+                                               "bf16"),
+        "varlen_rows_f32": lambda: W.varlen_batch("il_vf", 35, [1, 40, 1, 3],
+                                                  [600, 100, 1300, 517], 8, 2, 64, "f32"),
+    }[name]()
+    say("inline plan vs plan kernel", batch.name)
+    db = _device_batch(batch)
+    db.write_new()
+    monkeypatch.setenv("PA_DECODE_INLINE_PLAN", "0")
+    a = db.attend().clone()
+    monkeypatch.setenv("PA_DECODE_INLINE_PLAN", "1")
+    b = db.attend().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    if name in ("ragged_g8", "varlen_mixed"):
+        hs = host_state(batch)
+        want = expected(batch, hs)
+        if batch.kind == "decode":
+            err = _max_err(b, want)
+        else:
+            cu = batch.cu_seqlens
+            err = max(_max_err(b[int(cu[i]):int(cu[i + 1])], want[i]) for i in want)
+        say("max abs err", err)
+        assert err <= TOL[batch.dtype], err

@@ -69,6 +69,7 @@ def make_batch(name: str):
         "long_prefix_cascade": W.long_prefix_decode,
         "mixed_step": W.mixed_step,
         "prefill_chunks": W.prefill_only,
+        "prefill_long": W.prefill_long,
         "tiny_decode": W.tiny_decode,
     }[name]()
 
@@ -335,7 +336,7 @@ def main() -> int:
     ap.add_argument("--workload", default="llama2_decode",
                     choices=["llama2_decode", "gqa_decode", "shared_prefix_decode",
                              "shared_prefix_cascade", "long_prefix_decode",
-                             "long_prefix_cascade", "mixed_step", "prefill_chunks",
+                             "long_prefix_cascade", "mixed_step", "prefill_chunks", "prefill_long",
                              "tiny_decode", "block_swap"])
     ap.add_argument("--layers", type=int, default=0,
                     help="layer caches to rotate through (0: enough for >= 1 GiB)")

@@ -68,77 +68,128 @@ __device__ __forceinline__ int2* prefill_items(int32_t* work) {
 // they stream, most first (a counting sort in LDS), so the persistent
 // workgroups start the longest items first, on every CU at once.  The order
 // among equal counts is arbitrary: items are independent and each writes only
-// its own rows.
-__global__ __launch_bounds__(1024) void prefill_plan_kernel(PrefillArgs a, int tile_tokens) {
+// its own rows.  The work is spread over (sequence, query tile) pairs, so a
+// few long chunks do not leave one thread per sequence walking its tiles.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanMaxSeqs = 2048;  // sequences held in LDS (two per thread)
+
+__global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillArgs a,
+                                                                    int tile_tokens) {
   __shared__ int count[kSortBuckets];
-  __shared__ int wave_tot[1024 / 64];
+  __shared__ int wave_tot[kPlanThreads / 64];
+  __shared__ int pair0[kPlanMaxSeqs];  // first (sequence, query tile) pair of each sequence
+  __shared__ int slen[kPlanMaxSeqs], sctx[kPlanMaxSeqs];
   const int n = a.num_seqs;
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int maxk = max(0, min(a.max_context_len, a.max_blocks_per_seq * kBlockSize));
-  for (int i = t; i < kSortBuckets; i += blockDim.x) count[i] = 0;
-  // this thread's first sequence, read once (the common case: n <= 1024)
-  int len0 = 0, c0 = 0;
-  if (t < n) {
-    const int lo = a.cu_seqlens[t];
-    len0 = a.cu_seqlens[t + 1] - lo;
-    c0 = a.context_offsets[t];
-  }
-  __syncthreads();
-  auto seq_meta = [&](int s, int& len, int& c) {
-    if (s == t) {
-      len = len0;
-      c = c0;
-    } else {
-      len = a.cu_seqlens[s + 1] - a.cu_seqlens[s];
-      c = a.context_offsets[s];
+  for (int i = t; i < kSortBuckets; i += kPlanThreads) count[i] = 0;
+
+  // exclusive scan over the block of one value per thread; returns the
+  // thread's offset, and the sum in `total`
+  auto block_scan = [&](int v, int& total) -> int {
+    int inc = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int up = __shfl_up(inc, off);
+      if (lane >= off) inc += up;
     }
+    if (lane == 63) wave_tot[wave] = inc;
+    __syncthreads();
+    int base = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < kPlanThreads / 64; ++w) {
+      const int x = wave_tot[w];
+      base += w < wave ? x : 0;
+      total += x;
+    }
+    __syncthreads();  // wave_tot is reused by the next scan
+    return base + inc - v;
   };
   auto bucket = [&](int len, int c, int q) {
     const int qn = min(tile_tokens, len - q * tile_tokens);
     const int kend = max(0, min(c + q * tile_tokens + qn, maxk));
     return min(ceil_div(kend, kKeyTile), kSortBuckets - 1);
   };
-  for (int s = t; s < n; s += blockDim.x) {
-    int len, c;
-    seq_meta(s, len, c);
-    if (len < 2) continue;
-    const int nt = ceil_div(len, tile_tokens);
-    for (int q = 0; q < nt; ++q) atomicAdd(&count[bucket(len, c, q)], a.num_kv_heads);
+
+  // each thread: sequences 2t, 2t+1 (metadata into LDS) and their query tiles
+  const bool fits = n <= kPlanMaxSeqs;
+  int npairs = 0;
+  if (fits) {
+    int nt[2] = {0, 0};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int sq = 2 * t + j;
+      if (sq < n) {
+        const int lo = a.cu_seqlens[sq];
+        const int len = a.cu_seqlens[sq + 1] - lo;
+        slen[sq] = len;
+        sctx[sq] = a.context_offsets[sq];
+        nt[j] = len >= 2 ? ceil_div(len, tile_tokens) : 0;
+      }
+    }
+    const int first = block_scan(nt[0] + nt[1], npairs);
+    if (2 * t < n) pair0[2 * t] = first;
+    if (2 * t + 1 < n) pair0[2 * t + 1] = first + nt[0];
   }
   __syncthreads();
-  // exclusive offsets, largest bucket first: thread t owns bucket 1023 - t;
-  // inclusive scans inside each wave, then over the waves' totals
-  static_assert(kSortBuckets == 1024, "one bucket per thread");
-  const int mine = count[kSortBuckets - 1 - t];
-  int inc = mine;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int up = __shfl_up(inc, off);
-    if (lane >= off) inc += up;
+  // the sequence of pair p: the last s with pair0[s] <= p (sequences without
+  // tiles repeat their successor's start and are passed over)
+  auto seq_of = [&](int p) -> int {
+    int lo = 0, hi = n;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pair0[mid] <= p) lo = mid;
+      else hi = mid;
+    }
+    return lo;
+  };
+  auto seq_meta = [&](int sq, int& len, int& c) {
+    len = a.cu_seqlens[sq + 1] - a.cu_seqlens[sq];
+    c = a.context_offsets[sq];
+  };
+
+  if (fits) {
+    for (int p = t; p < npairs; p += kPlanThreads) {
+      const int sq = seq_of(p);
+      atomicAdd(&count[bucket(slen[sq], sctx[sq], p - pair0[sq])], a.num_kv_heads);
+    }
+  } else {
+    for (int sq = t; sq < n; sq += kPlanThreads) {
+      int len, c;
+      seq_meta(sq, len, c);
+      if (len < 2) continue;
+      const int nt = ceil_div(len, tile_tokens);
+      for (int q = 0; q < nt; ++q) atomicAdd(&count[bucket(len, c, q)], a.num_kv_heads);
+    }
   }
-  if (lane == 63) wave_tot[wave] = inc;
   __syncthreads();
-  int base = 0, total = 0;
-#pragma unroll
-  for (int w = 0; w < 1024 / 64; ++w) {
-    const int v = wave_tot[w];
-    base += w < wave ? v : 0;
-    total += v;
-  }
-  count[kSortBuckets - 1 - t] = base + inc - mine;
+  // exclusive offsets, largest bucket first: thread t owns bucket 1023 - t
+  static_assert(kSortBuckets == kPlanThreads, "one bucket per thread");
+  int total = 0;
+  const int off = block_scan(count[kSortBuckets - 1 - t], total);
+  count[kSortBuckets - 1 - t] = off;
   if (t == 0) a.work[0] = min(total, a.work_cap);
   __syncthreads();
   int2* items = prefill_items(a.work);
-  for (int s = t; s < n; s += blockDim.x) {
-    int len, c;
-    seq_meta(s, len, c);
-    if (len < 2) continue;
-    const int nt = ceil_div(len, tile_tokens);
-    for (int q = 0; q < nt; ++q) {
-      const int pos = atomicAdd(&count[bucket(len, c, q)], a.num_kv_heads);
-      for (int h = 0; h < a.num_kv_heads; ++h)
-        if (pos + h < a.work_cap) items[pos + h] = make_int2(s, q * a.num_kv_heads + h);
+  auto place = [&](int sq, int q, int len, int c) {
+    const int pos = atomicAdd(&count[bucket(len, c, q)], a.num_kv_heads);
+    for (int h = 0; h < a.num_kv_heads; ++h)
+      if (pos + h < a.work_cap) items[pos + h] = make_int2(sq, q * a.num_kv_heads + h);
+  };
+  if (fits) {
+    for (int p = t; p < npairs; p += kPlanThreads) {
+      const int sq = seq_of(p);
+      place(sq, p - pair0[sq], slen[sq], sctx[sq]);
+    }
+  } else {
+    for (int sq = t; sq < n; sq += kPlanThreads) {
+      int len, c;
+      seq_meta(sq, len, c);
+      if (len < 2) continue;
+      const int nt = ceil_div(len, tile_tokens);
+      for (int q = 0; q < nt; ++q) place(sq, q, len, c);
     }
   }
 }
@@ -586,7 +637,8 @@ static int prefill_cus() {
 
 template <int G>
 static hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(1024), 0, stream, a, prefill_tile_tokens(G));
+  hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a,
+                     prefill_tile_tokens(G));
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   static int per_cu = 0;

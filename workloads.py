@@ -354,6 +354,13 @@ def prefill_only(seed: int = 4, n_prefill: int = 8) -> PagedBatch:
     return varlen_batch("prefill_chunks_bf16", seed, chunk_len, chunk_ctx, 32, 8, 128, "bf16")
 
 
+def prefill_long(seed: int = 7, n: int = 4, chunk: int = 2048, cached: int = 2048) -> PagedBatch:
+    """Long prefill chunks: n sequences each bring `chunk` new tokens after
+    `cached` cached ones (32 q / 8 kv heads, d=128, bf16) -- items of up to 64
+    key tiles, where start-up and the longest-first tail weigh little."""
+    return varlen_batch("prefill_long_bf16", seed, [chunk] * n, [cached] * n, 32, 8, 128, "bf16")
+
+
 def shared_prefix_decode(seed: int = 5, n: int = 128, prefix_blocks: int = 64,
                          suffix_range=(16, 31744), unshared: bool = False,
                          num_q_heads: int = 32, num_kv_heads: int = 8, head_dim: int = 128,

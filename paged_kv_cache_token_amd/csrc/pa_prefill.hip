@@ -33,6 +33,7 @@
 //     on the way into LDS (p = 0 times a stale NaN would poison the sum).
 
 #include <math.h>
+#include <stdlib.h>
 
 #include <algorithm>
 
@@ -232,6 +233,14 @@ __device__ __forceinline__ uint2 lds_read_tr(const uint16_t* p) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(PA_LDS(i16x4_t, p)));
 }
 
+// A prefill work item's metadata, and the table entries of its first two key
+// tiles (one per lane, lane i: block i & 3 of the tile).
+struct ItemMeta {
+  int seq, qtile, kvh;  // cascade: key split, row tile, kv head
+  int lo_row, len, c;   // first packed row, query rows, cached tokens
+  int e0, e1;
+};
+
 // One work item.  Prefill (CASCADE = false): sequence `seq`, query tile
 // `qtile`, kv head `kvh`; rows are (q head, token) of the tile.  Common-prefix
 // pass (CASCADE = true): `seq` is the key split (tiles split*split_tiles ..),
@@ -239,8 +248,9 @@ __device__ __forceinline__ uint2 lds_read_tr(const uint16_t* p) {
 // sees the prefix keys below its own context length, and the item writes
 // unnormalised partials instead of the output.
 template <int G, bool CASCADE>
-__device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int qtile, int kvh,
+__device__ __forceinline__ void prefill_item(const PrefillArgs& a, const ItemMeta& im,
                                              PrefillShared& sm) {
+  const int seq = im.seq, qtile = im.qtile, kvh = im.kvh;
   constexpr int D = kPrefillD;
   constexpr int BMT = kPrefillRows / G;  // query tokens per item
   constexpr float kNegInf = -INFINITY;
@@ -257,9 +267,9 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int 
     len = a.num_seqs;
     c = 0;
   } else {
-    lo_row = __builtin_amdgcn_readfirstlane(a.cu_seqlens[seq]);
-    len = __builtin_amdgcn_readfirstlane(a.cu_seqlens[seq + 1]) - lo_row;
-    c = __builtin_amdgcn_readfirstlane(a.context_offsets[seq]);
+    lo_row = im.lo_row;
+    len = im.len;
+    c = im.c;
   }
   const int tile0 = CASCADE ? seq * a.split_tiles : 0;  // first key tile of the item
   const int q0 = qtile * BMT;
@@ -545,11 +555,14 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int 
     }
   };
 
+  // the previous item's last V reads (waves 4-7 read after the final barrier)
+  // are done before the first loads of this one refill buffers 0 and 1
+  __syncthreads();
   if (ntiles > 0) {
-    const int e0 = entries(0);
+    const int e0 = CASCADE ? entries(0) : im.e0;
     issue(0, 0, e0);
     bq = bad_mask(e0);
-    const int e1 = entries(1);
+    const int e1 = CASCADE ? entries(1) : im.e1;
     if (ntiles > 1) issue(1, 1, e1);
     bq |= bad_mask(e1) << 4;
     e2 = entries(2);
@@ -605,25 +618,43 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int seq, int 
   }
 }
 
+// The metadata and first table entries of work-list item `idx`, loaded
+// directly (a workgroup's first item).
+__device__ __forceinline__ ItemMeta load_item_meta(const PrefillArgs& a, int idx) {
+  const int2 w = prefill_items(a.work)[idx];
+  ItemMeta im;
+  im.seq = __builtin_amdgcn_readfirstlane(w.x);
+  const int y = __builtin_amdgcn_readfirstlane(w.y);
+  im.qtile = y / a.num_kv_heads;
+  im.kvh = y - im.qtile * a.num_kv_heads;
+  im.lo_row = __builtin_amdgcn_readfirstlane(a.cu_seqlens[im.seq]);
+  im.len = __builtin_amdgcn_readfirstlane(a.cu_seqlens[im.seq + 1]) - im.lo_row;
+  im.c = __builtin_amdgcn_readfirstlane(a.context_offsets[im.seq]);
+  const int lane = threadIdx.x & 63;
+  const int32_t* table = a.block_tables + (int64_t)im.seq * a.max_blocks_per_seq;
+  im.e0 = table[min(lane & 3, a.max_blocks_per_seq - 1)];
+  im.e1 = table[min(4 + (lane & 3), a.max_blocks_per_seq - 1)];
+  return im;
+}
+
+// Persistent workgroups walk the longest-first list.
 template <int G>
 __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a) {
   __shared__ PrefillShared sm;
   const int total = a.work[0];
-  const int2* items = prefill_items(a.work);
-  for (int it = blockIdx.x; it < total; it += gridDim.x) {
-    // the item is wave-uniform: keep it (and all that derives from it) scalar
-    const int2 w = items[it];
-    const int seq = __builtin_amdgcn_readfirstlane(w.x);
-    const int y = __builtin_amdgcn_readfirstlane(w.y);
-    prefill_item<G, false>(a, seq, y / a.num_kv_heads, y % a.num_kv_heads, sm);
-  }
+  for (int it = blockIdx.x; it < total; it += gridDim.x)
+    prefill_item<G, false>(a, load_item_meta(a, it), sm);
 }
 
 // Common-prefix pass: item (split, row tile, kv head) = (x, y, z).
 template <int G>
 __global__ __launch_bounds__(kPrefillThreads) void cascade_prefix_kernel(PrefillArgs a) {
   __shared__ PrefillShared sm;
-  prefill_item<G, true>(a, blockIdx.x, blockIdx.y, blockIdx.z, sm);
+  ItemMeta im{};
+  im.seq = blockIdx.x;
+  im.qtile = blockIdx.y;
+  im.kvh = blockIdx.z;
+  prefill_item<G, true>(a, im, sm);
 }
 
 static int prefill_cus() {
@@ -651,7 +682,11 @@ static hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t stream) {
       nb = 1;
     per_cu = nb;
   }
-  const int64_t want = (int64_t)2 * per_cu * prefill_cus();
+  // twice the resident workgroups: the dispatcher hands a freed CU the next
+  // one (tuning override PA_PREFILL_GRID, e.g. to give each workgroup many items)
+  int64_t want = (int64_t)2 * per_cu * prefill_cus();
+  const char* eg = getenv("PA_PREFILL_GRID");
+  if (eg && *eg && atoi(eg) >= 1) want = atoi(eg);
   const int gx = (int)std::max<int64_t>(1, std::min<int64_t>(a.work_cap, want));
   hipLaunchKernelGGL((prefill_kernel<G>), dim3(gx), dim3(kPrefillThreads), 0, stream, a);
   return hipGetLastError();

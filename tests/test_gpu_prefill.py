@@ -172,3 +172,19 @@ def test_varlen_rows_path(gpu, dtype, d, hq, hkv):
         err = max(err, float(np.abs(got[lo:hi] - rows).max()))
     say("max abs err", err)
     assert err <= tol, err
+
+
+@pytest.mark.parametrize("grid", ["1", "3", "17"])
+def test_prefill_many_items_per_workgroup(gpu, monkeypatch, grid):
+    """Persistent workgroups run several items each, reading each next item's
+    metadata during the current one: same output, bit for bit, as one item
+    per workgroup, and parity with the oracle."""
+    q_lens = [100, 70, 2, 129, 33, 64, 1, 250]
+    ctx = [0, 37, 5, 200, 64, 1000, 300, 17]
+    batch = W.varlen_batch(f"many_items_{grid}", 23, q_lens, ctx, 32, 8, 128, "bf16")
+    db, out = _check(batch)
+    ref = out.clone()
+    monkeypatch.setenv("PA_PREFILL_GRID", grid)
+    got = db.attend().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)

@@ -589,7 +589,11 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
 template <bool BF16, int D, int G, bool VARLEN, int NB>
 __global__ __launch_bounds__(256) void decode_direct_kernel(DecodeArgs a) {
   __shared__ DecodeShared<G, D> sm;
-  decode_item<BF16, D, G, VARLEN, NB>(a, blockIdx.x, 0, blockIdx.y, sm);
+  // kv head fastest: the workgroups of one sequence are dispatched together,
+  // so no kv head's share of the work is left to the end of the launch
+  const int hkv = a.num_kv_heads;
+  const int seq = blockIdx.x / hkv;
+  decode_item<BF16, D, G, VARLEN, NB>(a, seq, 0, blockIdx.x - seq * hkv, sm);
 }
 
 // One workgroup per (sequence, kv head, partition); partitions past a
@@ -701,7 +705,13 @@ __global__ __launch_bounds__(256) void decode_list_kernel(DecodeArgs a) {
     inline_plan<VARLEN>(a, plan_lds, plan_lds + a.num_seqs, total_full, total);
   else
     total = *a.ws.count;
-  for (int it = blockIdx.x; it < total; it += gridDim.x) {
+  // kv head fastest: item slot blockIdx.x / hkv, so the list's longest-first
+  // order holds across kv heads in dispatch order
+  const int hkv = a.num_kv_heads;
+  const int slot = blockIdx.x / hkv;
+  const int kvh = blockIdx.x - slot * hkv;
+  const int slots = gridDim.x / hkv;
+  for (int it = slot; it < total; it += slots) {
     int seq, part;
     if (a.inline_plan) {
       const int* ex_full = plan_lds;
@@ -719,7 +729,7 @@ __global__ __launch_bounds__(256) void decode_list_kernel(DecodeArgs a) {
       seq = w.x;
       part = w.y;
     }
-    decode_item<BF16, D, G, VARLEN, NB>(a, seq, part, blockIdx.y, sm);
+    decode_item<BF16, D, G, VARLEN, NB>(a, seq, part, kvh, sm);
   }
 }
 
@@ -784,7 +794,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   const dim3 block(64 * a.waves);
   if (a.max_parts <= 1) {
     hipLaunchKernelGGL((decode_direct_kernel<BF16, D, G, VARLEN, NB>),
-                       dim3(a.num_seqs, a.num_kv_heads), block, 0, stream, a);
+                       dim3((unsigned)a.num_seqs * a.num_kv_heads), block, 0, stream, a);
     return hipGetLastError();
   }
   hipError_t err;
@@ -820,8 +830,8 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   const int64_t items_bound = (int64_t)a.num_seqs * a.max_parts;
   const int gx = (int)std::max<int64_t>(
       1, std::min<int64_t>(items_bound, (want + a.num_kv_heads - 1) / a.num_kv_heads));
-  hipLaunchKernelGGL((decode_list_kernel<BF16, D, G, VARLEN, NB>), dim3(gx, a.num_kv_heads), block,
-                     plan_lds, stream, a);
+  hipLaunchKernelGGL((decode_list_kernel<BF16, D, G, VARLEN, NB>),
+                     dim3((unsigned)gx * a.num_kv_heads), block, plan_lds, stream, a);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((decode_merge_kernel<BF16, D, VARLEN>), dim3(a.num_q_heads, a.num_seqs),

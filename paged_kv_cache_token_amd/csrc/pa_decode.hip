@@ -898,6 +898,12 @@ void decode_config(int num_seqs, int num_kv_heads, int max_context_len, int* wav
   // ran 10% faster that way).
   int w = 4, pt = max_context_len >= 8192 ? 1024 : 512, nb = 2;
   const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
+  // Many short contexts: an item of a few blocks spreads them over fewer
+  // waves, which saves the cross-wave merge, and there are items enough to
+  // fill the chip (2048 sequences of 64 tokens, g=4: 116 us with one wave per
+  // item against 181 us with four; 1024 of 100 tokens: 98 against 115).
+  if (max_context_len <= 256 && pairs >= 8192) w = 1;
+  else if (max_context_len <= 512 && pairs >= 4096) w = 2;
   const int whole = ceil_div(max(max_context_len, 1), kBlockSize) * kBlockSize;
   if (pairs >= 4096 && whole <= kBlockSize * kMaxEntriesPerWave * w) pt = max(pt, whole);
   // tuning overrides; only values that keep every access in bounds are taken

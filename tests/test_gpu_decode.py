@@ -285,3 +285,35 @@ def test_inline_plan_equals_plan_kernel(gpu, monkeypatch, name):
             err = max(_max_err(b[int(cu[i]):int(cu[i + 1])], want[i]) for i in want)
         say("max abs err", err)
         assert err <= TOL[batch.dtype], err
+
+
+# ---- launch-shape variants ----------------------------------------------------
+
+@pytest.mark.parametrize("env", [
+    {"PA_DECODE_WAVES": "1"}, {"PA_DECODE_WAVES": "2"},
+    {"PA_DECODE_BUFFERS": "1"}, {"PA_DECODE_BUFFERS": "3"}, {"PA_DECODE_BUFFERS": "4"},
+    {"PA_DECODE_PARTITION": "256"}, {"PA_DECODE_PARTITION": "1024"},
+    {"PA_DECODE_GRID": "1"}, {"PA_DECODE_OVERSUB": "1"},
+    {"PA_DECODE_WAVES": "1", "PA_DECODE_PARTITION": "1024"},
+], ids=lambda e: ",".join(f"{k[10:].lower()}={v}" for k, v in e.items()))
+def test_decode_launch_variants(gpu, monkeypatch, env):
+    """Every launch shape the library can pick (waves per workgroup, register
+    buffers, partition length, grid or list) gives oracle parity."""
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    lens = [1, 2, 15, 16, 17, 100, 511, 512, 513, 1024, 1100, 2049]
+    for dtype, d, hq, hkv in (("bf16", 128, 32, 8), ("f32", 64, 8, 8)):
+        batch = W.decode_batch(f"variant_{dtype}", 36, lens, hq, hkv, d, dtype, pool_factor=1.3)
+        _check_decode(batch, check_pools=False)
+
+
+@pytest.mark.parametrize("n,max_len", [(1100, 256), (600, 500)])
+def test_decode_many_short_contexts(gpu, n, max_len):
+    """Batches of many short contexts run one or two waves per item (no
+    cross-wave merge for one): sampled rows against the oracle."""
+    rng = np.random.default_rng(37 + n)
+    lens = rng.integers(1, max_len + 1, size=n)
+    lens[0] = max_len
+    batch = W.decode_batch(f"short_{n}", 37, lens, 32, 8, 128, "bf16", pool_factor=1.2)
+    seqs = sorted(set([0, 1, n - 1] + rng.choice(n, size=40, replace=False).tolist()))
+    _check_decode(batch, seqs=seqs, check_pools=False)

@@ -317,3 +317,14 @@ def test_decode_many_short_contexts(gpu, n, max_len):
     batch = W.decode_batch(f"short_{n}", 37, lens, 32, 8, 128, "bf16", pool_factor=1.2)
     seqs = sorted(set([0, 1, n - 1] + rng.choice(n, size=40, replace=False).tolist()))
     _check_decode(batch, seqs=seqs, check_pools=False)
+
+
+def test_decode_list_beyond_inline_plan(gpu):
+    """More sequences than a workgroup derives its work list for (2048), with
+    a context long enough to need partitions: the plan-kernel path."""
+    rng = np.random.default_rng(38)
+    lens = rng.integers(1, 65, size=2100)
+    lens[7] = 5000
+    batch = W.decode_batch("list_2100", 38, lens, 32, 8, 128, "bf16", pool_factor=1.2)
+    seqs = sorted(set([0, 7, 2099] + rng.choice(2100, size=30, replace=False).tolist()))
+    _check_decode(batch, seqs=seqs, check_pools=False)

@@ -188,3 +188,18 @@ def test_prefill_many_items_per_workgroup(gpu, monkeypatch, grid):
     got = db.attend().clone()
     torch.cuda.synchronize()
     assert torch.equal(got, ref)
+
+
+def test_packed_call_beyond_plan_lds(gpu):
+    """A packed call of more sequences than the prefill plan holds in LDS
+    (2048): mostly decode rows, a few chunks; the plan's loop path."""
+    rng = np.random.default_rng(24)
+    n = 2100
+    q_lens = np.ones(n, dtype=np.int64)
+    chunk_at = [5, 900, 2099]
+    for i, L in zip(chunk_at, (70, 130, 33)):
+        q_lens[i] = L
+    ctx = rng.integers(0, 200, size=n)
+    batch = W.varlen_batch("plan_2100", 24, q_lens, ctx, 32, 8, 128, "bf16")
+    seqs = sorted(set(chunk_at + [0, 1, 2000] + rng.choice(n, size=20, replace=False).tolist()))
+    _check(batch, seqs=seqs)

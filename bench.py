@@ -328,6 +328,79 @@ def bench_block_swap(args, dev) -> int:
     return 0
 
 
+def bench_block_manager(args) -> int:
+    """The host block manager (pa_bm_*) on the LLaMA-2-7B-shaped decode
+    configuration: 64 running sequences (contexts U[128, 384], blocks from a
+    4096-block pool).  One step = allocate_batch (one new token for every
+    sequence), then build_step, which writes the decode step's block tables,
+    lengths and slot mapping.  Timed on the host through the binding (its per-call cost
+    included); build_step alone is reported beside.  No GPU work."""
+    import paged_kv_cache_token_amd as pa
+    rng = np.random.default_rng(2)
+    n, nb, maxb = 64, 4096, 64
+    ctx = rng.integers(128, 384 + 1, size=n)
+    bm = pa.BlockManager(nb)
+    for i, c in enumerate(ctx):
+        if not bm.allocate_slots(i, int(c)):
+            raise RuntimeError("pool too small for the initial contexts")
+    ids = np.arange(n, dtype=np.int64)
+    ql = np.ones(n, dtype=np.int32)
+
+    def step():
+        if bm.allocate_batch(ids, ql) != n:
+            raise RuntimeError("pool exhausted")
+        return bm.build_step(ids, ql, maxb)
+
+    for _ in range(args.warmup):
+        step()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        meta = step()
+    wall = time.perf_counter() - t0
+    s_per_step = wall / args.steps
+    t1 = time.perf_counter()
+    reps = 200
+    for _ in range(reps):
+        bm.build_step(ids, ql, maxb)
+    build_us = (time.perf_counter() - t1) / reps * 1e6
+    # the same allocation with one binding call per sequence, for comparison
+    t3 = time.perf_counter()
+    for _ in range(20):
+        for i in range(n):
+            bm.allocate_slots(i, 1)
+    one_by_one_us = (time.perf_counter() - t3) / 20 * 1e6
+    cpu = None
+    if not args.no_cpu_baseline:
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        import oracle
+        bt, cu, co = meta["block_tables"], meta["cu_seqlens"], meta["context_offsets"]
+        t2, c2, k = time.perf_counter(), time.process_time(), 0
+        while time.perf_counter() - t2 < 2.0:
+            oracle.slot_mapping(bt, cu, co)
+            k += 1
+        w2 = time.perf_counter() - t2
+        cpu = {"value": round(k * n / w2, 1), "unit": "seq-steps/s",
+               "cores": max(1, int(round((time.process_time() - c2) / w2))), "kind": "oracle",
+               "sample": f"oracle slot mapping of the same step's tables, {k} passes in {w2:.1f} s"}
+    rec = {
+        "metric": METRIC, "value": round(n / s_per_step, 1), "unit": "seq-steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(s_per_step * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int64",
+        "data": "synthetic",
+        "config": {"workload": "block_manager_llama2_decode", "num_seqs": n, "pool_blocks": nb,
+                   "block_size": 16, "context_min_max": [int(ctx.min()), int(ctx.max())],
+                   "parallelism": "host"},
+        "roofline": None,
+        "roofline_note": "host code, no GPU kernel: the figure is host time per step",
+        "cpu_baseline": cpu,
+        "build_step_us": round(build_us, 2),
+        "allocate_slots_one_call_per_sequence_us": round(one_by_one_us, 2),
+        "step_calls": "pa_bm_allocate_batch + pa_bm_build_step",
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -337,7 +410,7 @@ def main() -> int:
                     choices=["llama2_decode", "gqa_decode", "shared_prefix_decode",
                              "shared_prefix_cascade", "long_prefix_decode",
                              "long_prefix_cascade", "mixed_step", "prefill_chunks", "prefill_long",
-                             "tiny_decode", "block_swap"])
+                             "tiny_decode", "block_swap", "block_manager"])
     ap.add_argument("--layers", type=int, default=0,
                     help="layer caches to rotate through (0: enough for >= 1 GiB)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -360,6 +433,8 @@ def main() -> int:
     import paged_kv_cache_token_amd as pa  # fails loudly if libpa.so is missing
     from device_batch import DeviceBatch
 
+    if args.workload == "block_manager":
+        return bench_block_manager(args)  # host code only
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         return 2

@@ -82,6 +82,22 @@ int32_t pa_bm_allocate_slots(pa_block_manager* bm, int64_t seq_id, int32_t num_n
                              int32_t num_lookahead_tokens);
 
 /*
+ * pa_bm_allocate_batch -- pa_bm_allocate_slots for seq_ids[i] with
+ * num_new_tokens[i], i = 0 .. num_seqs-1 in order (one scheduling step in one
+ * call), stopping at the first sequence the free queue cannot serve.
+ * *num_served receives how many were served; those before it are allocated
+ * exactly as by pa_bm_allocate_slots, nothing is taken for the rest.
+ *
+ * Returns PA_OK when all were served, PA_ERR_NO_FREE_BLOCKS when the queue ran
+ * short at sequence *num_served (the caller may preempt and retry from
+ * there), PA_ERR_INVALID_ARGUMENT for an invalid count (at *num_served, the
+ * earlier ones served), PA_ERR_NULL_POINTER for NULL arrays.
+ */
+int32_t pa_bm_allocate_batch(pa_block_manager* bm, const int64_t* seq_ids,
+                             const int32_t* num_new_tokens, int32_t num_seqs,
+                             int32_t num_lookahead_tokens, int32_t* num_served);
+
+/*
  * pa_bm_share_prefix -- start sequence dst_seq (which must not exist) on the
  * first num_tokens tokens of src_seq by reference ([KW] §1.3 read-only
  * sharing of a common prefix).  Only whole blocks are shared: dst_seq gets

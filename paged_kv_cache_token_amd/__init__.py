@@ -20,6 +20,7 @@ INCLUDE_DIR = os.path.join(os.path.dirname(_HERE), "include")
 HEADER_PATH = os.path.join(INCLUDE_DIR, "pa.h")
 
 PA_F32, PA_BF16 = 0, 1
+PA_ERR_NO_FREE_BLOCKS = 6
 BLOCK_SIZE = 16
 _DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
 
@@ -52,6 +53,7 @@ _SIGNATURES = {
     "pa_bm_destroy": (None, [_c_p]),
     "pa_bm_num_free_blocks": (_c_i64, [_c_p]),
     "pa_bm_allocate_slots": (_c_i32, [_c_p, _c_i64, _c_i32, _c_i32]),
+    "pa_bm_allocate_batch": (_c_i32, [_c_p, _c_p, _c_p, _c_i32, _c_i32, ctypes.POINTER(_c_i32)]),
     "pa_bm_share_prefix": (_c_i32, [_c_p, _c_i64, _c_i64, _c_i32]),
     "pa_bm_free_sequence": (_c_i32, [_c_p, _c_i64]),
     "pa_bm_sequence_info": (_c_i32, [_c_p, _c_i64, ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i32)]),
@@ -384,10 +386,25 @@ class BlockManager:
         too short (nothing changed)."""
         st = lib.pa_bm_allocate_slots(self._h, int(seq_id), int(num_new_tokens),
                                       int(num_lookahead_tokens))
-        if st == 6:  # PA_ERR_NO_FREE_BLOCKS
+        if st == PA_ERR_NO_FREE_BLOCKS:
             return False
         _check("pa_bm_allocate_slots", st)
         return True
+
+    def allocate_batch(self, seq_ids, num_new_tokens, num_lookahead_tokens: int = 0) -> int:
+        """allocate_slots for each sequence in order, in one call; returns how
+        many were served (all of them unless the free queue ran short)."""
+        import numpy as np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        nt = np.ascontiguousarray(num_new_tokens, dtype=np.int32)
+        if ids.shape != nt.shape or ids.ndim != 1:
+            raise ValueError("seq_ids and num_new_tokens must be 1-D of one length")
+        served = _c_i32(0)
+        st = lib.pa_bm_allocate_batch(self._h, ids.ctypes.data, nt.ctypes.data, ids.shape[0],
+                                      int(num_lookahead_tokens), ctypes.byref(served))
+        if st not in (0, PA_ERR_NO_FREE_BLOCKS):
+            _check("pa_bm_allocate_batch", st)
+        return int(served.value)
 
     def share_prefix(self, src_seq: int, dst_seq: int, num_tokens: int) -> None:
         _check("pa_bm_share_prefix", lib.pa_bm_share_prefix(self._h, int(src_seq), int(dst_seq),
@@ -434,6 +451,7 @@ class BlockManager:
                 "context_lens": cl[:n], "slot_mapping": sm[:total]}
 
 
-__all__ = ["BlockManager", "PAError", "swap_blocks", "PA_F32", "PA_BF16", "BLOCK_SIZE", "build_slot_mapping", "decode",
-           "decode_step", "decode_workspace_size", "header_functions", "lib", "status_string",
-           "varlen_prefill", "varlen_workspace_size", "version", "write_kv"]
+__all__ = ["BlockManager", "PAError", "swap_blocks", "PA_F32", "PA_BF16", "BLOCK_SIZE", "build_slot_mapping",
+           "cascade_decode", "cascade_workspace_size", "decode", "decode_step",
+           "decode_workspace_size", "header_functions", "lib", "status_string", "varlen_prefill",
+           "varlen_workspace_size", "version", "write_kv"]

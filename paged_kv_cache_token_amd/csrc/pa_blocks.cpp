@@ -90,6 +90,21 @@ int32_t pa_bm_allocate_slots(pa_block_manager* bm, int64_t seq_id, int32_t num_n
   return PA_OK;
 }
 
+int32_t pa_bm_allocate_batch(pa_block_manager* bm, const int64_t* seq_ids,
+                             const int32_t* num_new_tokens, int32_t num_seqs,
+                             int32_t num_lookahead_tokens, int32_t* num_served) {
+  if (!bm || !num_served) return PA_ERR_NULL_POINTER;
+  *num_served = 0;
+  if (num_seqs < 0) return PA_ERR_INVALID_ARGUMENT;
+  if (num_seqs > 0 && (!seq_ids || !num_new_tokens)) return PA_ERR_NULL_POINTER;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const int32_t st = pa_bm_allocate_slots(bm, seq_ids[i], num_new_tokens[i], num_lookahead_tokens);
+    if (st != PA_OK) return st;
+    *num_served = i + 1;
+  }
+  return PA_OK;
+}
+
 int32_t pa_bm_share_prefix(pa_block_manager* bm, int64_t src_seq, int64_t dst_seq,
                            int32_t num_tokens) {
   if (!bm) return PA_ERR_NULL_POINTER;

@@ -60,6 +60,33 @@ def test_failed_allocation_changes_nothing():
         bm.info(2)                            # the refused sequence was not created
 
 
+def test_allocate_batch_equals_one_by_one():
+    """pa_bm_allocate_batch serves sequences in order exactly as one call per
+    sequence, and stops at the first the free queue cannot serve, leaving it
+    and the rest untouched."""
+    rng = np.random.default_rng(9)
+    ids = [5, 1, 9, 2, 7, 3]
+    new = rng.integers(1, 40, size=len(ids))
+    a, b = pa.BlockManager(64), pa.BlockManager(64)
+    assert a.allocate_batch(ids, new) == len(ids)
+    for i, k in zip(ids, new):
+        assert b.allocate_slots(i, int(k))
+    for i in ids:
+        assert a.info(i) == b.info(i) and list(a.block_table(i)) == list(b.block_table(i))
+    assert a.num_free_blocks == b.num_free_blocks
+    # a short queue: 3 free blocks, asks of 1, 2, 2 blocks -> the first two served
+    c = pa.BlockManager(3)
+    assert c.allocate_batch([0, 1, 2], [16, 17, 20]) == 2
+    assert c.info(0) == (16, 1) and c.info(1) == (17, 2) and c.num_free_blocks == 0
+    with pytest.raises(pa.PAError):
+        c.info(2)
+    assert c.allocate_batch([], []) == 0
+    d = pa.BlockManager(8)
+    with pytest.raises(pa.PAError):
+        d.allocate_batch([0, 1], [1, -1])    # an invalid count: the ones before it are served
+    assert d.info(0) == (1, 1) and d.num_free_blocks == 7
+
+
 def test_free_returns_blocks_fifo():
     bm = pa.BlockManager(6)
     assert bm.allocate_slots(1, 32)           # blocks 0, 1

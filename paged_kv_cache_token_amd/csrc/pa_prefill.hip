@@ -498,7 +498,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const ItemMet
     // The next tile's score products (past the last tile they read a stale
     // buffer and are discarded), interleaved one for one with this tile's
     // exponentials so the matrix core and the vector ALU work at once; the
-    // K reads run two products ahead.  sched_barrier keeps this order.
+    // K reads run three products ahead.  sched_barrier keeps this order.
     const float moff = -((m == kNegInf) ? 0.f : m) * sl2;
     float ps[4] = {0.f, 0.f, 0.f, 0.f};  // partial row sums (independent chains)
     uint32_t pf[16];  // P^T pairs: pf[8u + 4t2 + e/2] = scores 8t2 + e, +1 of half u
@@ -507,17 +507,18 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const ItemMet
       return __builtin_bit_cast(bf16x8_t,
                                 sm.k[bn][2 * u + (n >> 4)][ch][(n & 15) ^ (4 * (ch & 3))]);
     };
-    bf16x8_t kq[3];
+    bf16x8_t kq[4];
     kq[0] = kread(0);
     kq[1] = kread(1);
+    kq[2] = kread(2);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      if (i + 2 < 16) kq[(i + 2) % 3] = kread(i + 2);
+      if (i + 3 < 16) kq[(i + 3) % 4] = kread(i + 3);
       const int u = i >> 3, ks = i & 7;
       if (ks == 0)
 #pragma unroll
         for (int r = 0; r < 16; ++r) nxt[u][r] = 0.f;
-      nxt[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[i % 3], qf[ks], nxt[u], 0, 0, 0);
+      nxt[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[i % 4], qf[ks], nxt[u], 0, 0, 0);
       const int r = 2 * (i & 7);
       const float p0 = fast_exp2(fmaf(cur[u][r], sl2, moff));
       const float p1 = fast_exp2(fmaf(cur[u][r + 1], sl2, moff));
@@ -534,18 +535,19 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const ItemMet
     }
 
     // O^T += V^T P^T; k step ut = 2u + t2 covers keys 16ut + {8(e/4) + 4hi + e%4};
-    // the V reads run two products ahead
+    // the V reads run three products ahead
     auto vread = [&](int j) -> bf16x8_t { return v_frag(bc, 16 * (j >> 2), j & 3); };
-    bf16x8_t vq[3];
+    bf16x8_t vq[4];
     vq[0] = vread(0);
     vq[1] = vread(1);
+    vq[2] = vread(2);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      if (j + 2 < 16) vq[(j + 2) % 3] = vread(j + 2);
+      if (j + 3 < 16) vq[(j + 3) % 4] = vread(j + 3);
       const int ut = j >> 2, dt = j & 3;
       const bf16x8_t pb = __builtin_bit_cast(
           bf16x8_t, make_uint4(pf[4 * ut], pf[4 * ut + 1], pf[4 * ut + 2], pf[4 * ut + 3]));
-      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vq[j % 3], pb, o[dt], 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vq[j % 4], pb, o[dt], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     bq >>= 4;

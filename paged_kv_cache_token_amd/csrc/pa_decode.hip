@@ -35,15 +35,19 @@
 //     combines the sequence's partitions in ascending order and writes `out`
 //     (a separate launch: the kernel boundary publishes the partials to every
 //     XCD, which inside one kernel would take an L2 write-back per item);
-//   * when every context fits one partition the grid is (sequence, kv head);
-//     otherwise a one-workgroup plan kernel lists the (sequence, partition)
-//     items and a persistent grid sized to the chip walks the list.
+//   * when every context fits one partition the grid is (sequence, kv head),
+//     kv head fastest; otherwise a persistent grid sized to the chip walks the
+//     (sequence, partition) list, full partitions first, which each workgroup
+//     derives from the lengths at its start (a one-workgroup plan kernel
+//     writes it instead past 2048 sequences);
+//   * a cascade decode's common prefix arrives as partials written by the
+//     matrix-core pass: the partitions start after it (key_start) and their
+//     slots follow its slots (prefix_parts), so the merge combines all.
 // The order of every sum depends only on logical token positions, never on the
 // physical block ids, so the output is
 // bit-identical under any placement or sharing of blocks and between runs.
 
 #include <math.h>
-
 #include <stdlib.h>
 
 #include <algorithm>

@@ -16,9 +16,10 @@
 //     32 rows per wave, 8 waves (two per SIMD, so one wave's softmax overlaps
 //     the other's matrix products), and each K/V tile read serves all g heads;
 //   * keys stream in tiles of 64 (4 physical blocks), gathered through the
-//     block table into double-buffered LDS: K row-major [key][dim], V
-//     transposed [dim][key].  One barrier per tile: tile t is computed while
-//     tile t+1 is staged and the loads of tile t+2 are in flight;
+//     block table straight from HBM into four LDS buffers (K and V alike as
+//     [block][16-byte chunk][key], keys swizzled by chunk; V is read back with
+//     the transposing LDS read).  One barrier per tile: tile t is computed
+//     while tile t+1 waits in LDS and the loads of tile t+2 are in flight;
 //   * the work list is ordered longest first (key tiles per item);
 //   * scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = the wave's 32 query rows
@@ -30,7 +31,10 @@
 //     operand reads V^T rows from LDS in that same key order;
 //   * the causal mask (key <= context_offset + row) is applied only on tiles
 //     that cross the diagonal; V of keys past the chunk's last key is zeroed
-//     on the way into LDS (p = 0 times a stale NaN would poison the sum).
+//     on the way into LDS (p = 0 times a stale NaN would poison the sum);
+//   * the same item code serves the common-prefix pass of a cascade decode:
+//     rows are the single query rows of 256/g sequences, keys a range of the
+//     shared prefix, and the item writes partial results for the decode merge.
 
 #include <math.h>
 #include <stdlib.h>

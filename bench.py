@@ -221,7 +221,18 @@ def context_figures(dbs, run_step, stream, steps, dev) -> dict:
     z.record(stream)
     torch.cuda.synchronize()
     out["copy_gbs_read_plus_write"] = round(2 * n * reps / (a.elapsed_time(z) * 1e-3) / 1e9, 1)
-    del src, dst
+    # a read-only stream (a sum over 1 GiB of fp32): the nearest plain
+    # figure to a decode kernel's traffic, which is almost all reads
+    x = src.view(torch.float32)
+    x.sum()
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        x.sum()
+    z.record(stream)
+    torch.cuda.synchronize()
+    out["read_gbs_sum_1gib"] = round(n * reps / (a.elapsed_time(z) * 1e-3) / 1e9, 1)
+    del src, dst, x
 
     try:
         side = torch.cuda.Stream()

@@ -108,6 +108,12 @@ def test_prefill_only_config(gpu):
     _check(W.prefill_only())
 
 
+def test_prefill_long_one_sequence(gpu):
+    """The long-chunk workload (4 x 2048 new tokens after 2048 cached, the
+    benchmark's launch): one whole sequence against the oracle."""
+    _check(W.prefill_long(), seqs=[2])
+
+
 def test_mixed_step_full_sampled(gpu):
     batch = W.mixed_step()
     n_dec = batch.notes["n_decode_rows"]

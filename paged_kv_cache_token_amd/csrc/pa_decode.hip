@@ -51,6 +51,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "../../include/pa.h"
 #include "pa_launch.h"
@@ -819,18 +820,22 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  static int per_cu[kDecodeMaxWaves + 1] = {0, 0, 0, 0, 0};
-  if (per_cu[a.waves] == 0) {
+  // resident workgroups per CU of this instance, per wave count (computed once;
+  // concurrent first calls compute the same value)
+  static std::atomic<int> per_cu[kDecodeMaxWaves + 1];
+  int resident = per_cu[a.waves].load(std::memory_order_relaxed);
+  if (resident == 0) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &nb, reinterpret_cast<const void*>(&decode_list_kernel<BF16, D, G, VARLEN, NB>),
             64 * a.waves, 0) != hipSuccess ||
         nb <= 0)
       nb = 2;
-    per_cu[a.waves] = nb;
+    resident = nb;
+    per_cu[a.waves].store(nb, std::memory_order_relaxed);
   }
   // a multiple of the resident capacity, so a finished workgroup's slot is refilled
-  const int64_t want = (int64_t)a.oversub * per_cu[a.waves] * device_cus();
+  const int64_t want = (int64_t)a.oversub * resident * device_cus();
   const int64_t items_bound = (int64_t)a.num_seqs * a.max_parts;
   const int gx = (int)std::max<int64_t>(
       1, std::min<int64_t>(items_bound, (want + a.num_kv_heads - 1) / a.num_kv_heads));

@@ -40,6 +40,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "pa_launch.h"
 
@@ -678,7 +679,10 @@ static hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t stream) {
                      prefill_tile_tokens(G));
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  static int per_cu = 0;
+  // resident workgroups per CU (computed once; concurrent first calls compute
+  // the same value)
+  static std::atomic<int> per_cu_cache{0};
+  int per_cu = per_cu_cache.load(std::memory_order_relaxed);
   if (per_cu == 0) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
@@ -687,6 +691,7 @@ static hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t stream) {
         nb <= 0)
       nb = 1;
     per_cu = nb;
+    per_cu_cache.store(nb, std::memory_order_relaxed);
   }
   // twice the resident workgroups: the dispatcher hands a freed CU the next
   // one (tuning override PA_PREFILL_GRID, e.g. to give each workgroup many items)

@@ -1,6 +1,6 @@
-"""HIP-graph capture of the hot path: a decode step (pa_decode_step) and a
-packed prefill call (slot mapping + write + pa_varlen_prefill) are captured
-once and replayed several times, with eager work and synchronisation between
+"""HIP-graph capture of the hot path: a decode step (pa_decode_step), a
+packed prefill call (slot mapping + write + pa_varlen_prefill) and a cascade
+decode are captured once and replayed several times, with eager work and synchronisation between
 replays; every replay must equal the eager result bit for bit (the library
 allocates nothing, synchronises nothing and records no memset, so a captured
 call is the same launches)."""
@@ -78,3 +78,13 @@ def test_graph_mixed_step(gpu):
         db.write_new()
         return db.attend(out)
     _replays(W.mixed_step, run)
+
+
+def test_graph_cascade_decode(gpu):
+    # the common-prefix pass, the decode kernels over the private parts and
+    # the merge, captured together
+    def run(db, out=None):
+        db.write_new()
+        return db.cascade(out)
+    _replays(lambda: W.shared_prefix_decode(seed=58, n=70, prefix_blocks=20,
+                                            suffix_range=(1, 1500)), run)

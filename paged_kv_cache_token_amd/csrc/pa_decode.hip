@@ -544,8 +544,10 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int seq, int pa
 template <bool BF16, int D, bool VARLEN>
 __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
   constexpr float kNegInf = -INFINITY;
-  const int h = blockIdx.x;
-  const int seq = blockIdx.y;
+  // one workgroup per (sequence, q head), q head fastest (a 1-D grid: packed
+  // calls taken row by row can have more rows than a grid's y extent)
+  const int seq = blockIdx.x / a.num_q_heads;
+  const int h = blockIdx.x - seq * a.num_q_heads;
   int qrow, ctx;
   if (!decode_row<VARLEN>(a, seq, qrow, ctx)) return;
   const int nparts = a.prefix_parts + parts_of(ctx - a.key_start, a.part_tokens);
@@ -808,7 +810,8 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
                        dim3(a.num_seqs, a.num_kv_heads, a.max_parts), block, 0, stream, a);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((decode_merge_kernel<BF16, D, VARLEN>), dim3(a.num_q_heads, a.num_seqs),
+    hipLaunchKernelGGL((decode_merge_kernel<BF16, D, VARLEN>),
+                       dim3((unsigned)a.num_q_heads * a.num_seqs),
                        dim3(D), 0, stream, a);
     return hipGetLastError();
   }
@@ -843,7 +846,8 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
                      dim3((unsigned)gx * a.num_kv_heads), block, plan_lds, stream, a);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((decode_merge_kernel<BF16, D, VARLEN>), dim3(a.num_q_heads, a.num_seqs),
+  hipLaunchKernelGGL((decode_merge_kernel<BF16, D, VARLEN>),
+                       dim3((unsigned)a.num_q_heads * a.num_seqs),
                      dim3(D), 0, stream, a);
   return hipGetLastError();
 }

@@ -209,3 +209,16 @@ def test_packed_call_beyond_plan_lds(gpu):
     batch = W.varlen_batch("plan_2100", 24, q_lens, ctx, 32, 8, 128, "bf16")
     seqs = sorted(set(chunk_at + [0, 1, 2000] + rng.choice(n, size=20, replace=False).tolist()))
     _check(batch, seqs=seqs)
+
+
+def test_packed_call_more_rows_than_grid_y(gpu):
+    """70000 single-token rows, one of them with a context long enough to be
+    split: the merge runs over more (row, head) pairs than a grid's y extent
+    holds (its grid is 1-D)."""
+    rng = np.random.default_rng(25)
+    n = 70000
+    ctx = rng.integers(0, 4, size=n)
+    ctx[123] = 5000
+    batch = W.varlen_batch("rows_70000", 25, np.ones(n, dtype=np.int64), ctx, 8, 1, 128, "bf16")
+    seqs = sorted(set([0, 123, n - 1] + rng.choice(n, size=30, replace=False).tolist()))
+    _check(batch, seqs=seqs)

@@ -105,7 +105,8 @@ const char* pa_status_string(int32_t status);
  *
  * slot = block_tables[i][pos / block_size] * block_size + pos % block_size.
  * A position whose logical block is past max_blocks_per_seq gets slot -1
- * (stored nowhere by pa_write_kv).
+ * (stored nowhere by pa_write_kv).  Token indices that inconsistent
+ * cu_seqlens place outside [0, num_tokens) are not written.
  */
 int32_t pa_build_slot_mapping(int64_t* slot_mapping, const int32_t* cu_seqlens,
                               const int32_t* context_offsets, const int32_t* block_tables,

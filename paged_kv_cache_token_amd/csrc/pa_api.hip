@@ -103,7 +103,7 @@ int32_t pa_build_slot_mapping(int64_t* slot_mapping, const int32_t* cu_seqlens,
   if (!slot_mapping || !cu_seqlens || !context_offsets || !block_tables) return PA_ERR_NULL_POINTER;
   if (max_blocks_per_seq == 0) return PA_ERR_INVALID_ARGUMENT;
   return from_hip(launch_slot_mapping(slot_mapping, cu_seqlens, context_offsets, block_tables,
-                                      num_seqs, max_blocks_per_seq,
+                                      num_seqs, max_blocks_per_seq, num_tokens,
                                       static_cast<hipStream_t>(stream)));
 }
 

@@ -9,7 +9,8 @@ namespace pa {
 
 hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* cu_seqlens,
                                const int32_t* context_offsets, const int32_t* block_tables,
-                               int32_t num_seqs, int32_t max_blocks_per_seq, hipStream_t stream);
+                               int32_t num_seqs, int32_t max_blocks_per_seq, int64_t num_tokens,
+                               hipStream_t stream);
 
 hipError_t launch_swap_blocks(void* dst, const void* src, const int64_t* pairs, int64_t num_pairs,
                               int64_t block_bytes, int64_t dst_blocks, int64_t src_blocks,

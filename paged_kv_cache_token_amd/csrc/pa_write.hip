@@ -16,17 +16,19 @@
 
 namespace pa {
 
-// One workgroup per sequence; lanes walk that sequence's new tokens.
+// One workgroup per sequence; lanes walk that sequence's new tokens.  Token
+// indices outside [0, num_tokens) (inconsistent cu_seqlens) are not written.
 __global__ __launch_bounds__(256) void slot_mapping_kernel(
     int64_t* __restrict__ slot_mapping, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ context_offsets, const int32_t* __restrict__ block_tables,
-    int32_t max_blocks_per_seq) {
+    int32_t max_blocks_per_seq, int64_t num_tokens) {
   const int seq = blockIdx.x;
   const int lo = cu_seqlens[seq];
-  const int hi = cu_seqlens[seq + 1];
+  const int hi = (int)min((int64_t)cu_seqlens[seq + 1], num_tokens);
   const int base = context_offsets[seq];
   const int32_t* table = block_tables + (int64_t)seq * max_blocks_per_seq;
   for (int t = lo + (int)threadIdx.x; t < hi; t += blockDim.x) {
+    if (t < 0) continue;
     const int pos = base + (t - lo);
     const int logical = pos / kBlockSize;
     int64_t slot = -1;
@@ -61,10 +63,11 @@ __global__ __launch_bounds__(256) void write_kv_kernel(
 
 hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* cu_seqlens,
                                const int32_t* context_offsets, const int32_t* block_tables,
-                               int32_t num_seqs, int32_t max_blocks_per_seq, hipStream_t stream) {
+                               int32_t num_seqs, int32_t max_blocks_per_seq, int64_t num_tokens,
+                               hipStream_t stream) {
   if (num_seqs == 0) return hipSuccess;
   hipLaunchKernelGGL(slot_mapping_kernel, dim3(num_seqs), dim3(256), 0, stream, slot_mapping,
-                     cu_seqlens, context_offsets, block_tables, max_blocks_per_seq);
+                     cu_seqlens, context_offsets, block_tables, max_blocks_per_seq, num_tokens);
   return hipGetLastError();
 }
 

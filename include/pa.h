@@ -80,7 +80,8 @@ typedef enum pa_status {
   PA_ERR_INVALID_ARGUMENT = 3,    /* negative or inconsistent count */
   PA_ERR_WORKSPACE_TOO_SMALL = 4, /* workspace_bytes below the size query */
   PA_ERR_HIP = 5,                 /* the HIP runtime refused a launch */
-  PA_ERR_NO_FREE_BLOCKS = 6       /* block manager: the free queue is too short */
+  PA_ERR_NO_FREE_BLOCKS = 6,      /* block manager: the free queue is too short */
+  PA_ERR_HOST_MEMORY = 7          /* block manager: a host allocation failed */
 } pa_status;
 
 /* Library version as PA_VERSION. */

@@ -35,7 +35,10 @@
  *     its front, freed blocks join its back.
  *   - Sequence ids are caller-chosen int64 values.
  *   - Return value: PA_OK or a pa_status (include/pa.h).  A call that fails
- *     changes nothing.
+ *     changes nothing.  The free queue is sized to the pool at creation;
+ *     pa_bm_create, pa_bm_allocate_slots (a new sequence or a longer block
+ *     list) and pa_bm_share_prefix allocate host memory and return
+ *     PA_ERR_HOST_MEMORY if that fails.  No C++ exception leaves a call.
  */
 #ifndef PA_BLOCKS_H_
 #define PA_BLOCKS_H_

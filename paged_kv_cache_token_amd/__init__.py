@@ -21,6 +21,7 @@ HEADER_PATH = os.path.join(INCLUDE_DIR, "pa.h")
 
 PA_F32, PA_BF16 = 0, 1
 PA_ERR_NO_FREE_BLOCKS = 6
+PA_ERR_HOST_MEMORY = 7
 BLOCK_SIZE = 16
 _DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
 
@@ -451,7 +452,8 @@ class BlockManager:
                 "context_lens": cl[:n], "slot_mapping": sm[:total]}
 
 
-__all__ = ["BlockManager", "PAError", "swap_blocks", "PA_F32", "PA_BF16", "BLOCK_SIZE", "build_slot_mapping",
+__all__ = ["BlockManager", "PAError", "swap_blocks", "PA_F32", "PA_BF16", "PA_ERR_NO_FREE_BLOCKS",
+           "PA_ERR_HOST_MEMORY", "BLOCK_SIZE", "build_slot_mapping",
            "cascade_decode", "cascade_workspace_size", "decode", "decode_step",
            "decode_workspace_size", "header_functions", "lib", "status_string", "varlen_prefill",
            "varlen_workspace_size", "version", "write_kv"]

@@ -89,6 +89,7 @@ const char* pa_status_string(int32_t status) {
     case PA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than the size query returned";
     case PA_ERR_HIP: return "the HIP runtime rejected a kernel launch";
     case PA_ERR_NO_FREE_BLOCKS: return "not enough free blocks in the pool";
+    case PA_ERR_HOST_MEMORY: return "a host memory allocation failed";
     default: return "unknown status";
   }
 }

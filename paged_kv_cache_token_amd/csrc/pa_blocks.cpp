@@ -10,13 +10,18 @@
 // of common blocks), §2.1 (a finished request's blocks return at once).
 //
 // Plain C++17 on the host: a FIFO of free block ids, a reference count per
-// block, and per sequence its block list and token count.
+// block, and per sequence its block list and token count.  The FIFO is a ring
+// sized to the pool when the manager is made, so taking and returning blocks
+// never allocates; the calls that do allocate (a new sequence, a longer block
+// list) do so before they change anything, and no C++ exception leaves the
+// library: a failed host allocation returns PA_ERR_HOST_MEMORY with the
+// manager as it was.
 
 #include <cstdint>
-#include <deque>
 #include <limits>
 #include <new>
 #include <unordered_map>
+#include <utility>
 #include <vector>
 
 #include "pa_blocks.h"
@@ -27,11 +32,27 @@ struct pa_block_manager {
     int64_t tokens = 0;           // tokens stored (the last block may be partial)
   };
   int32_t block_size = PA_BLOCK_SIZE;
-  std::deque<int32_t> free_queue;
+  // free-block FIFO: ring[(head + i) % capacity] for i < free_count
+  std::vector<int32_t> ring;
+  int64_t head = 0, free_count = 0;
   std::vector<int32_t> refcount;  // per physical block; 0 = in the free queue
   std::unordered_map<int64_t, Sequence> seqs;
 
   int64_t blocks_for(int64_t tokens) const { return (tokens + block_size - 1) / block_size; }
+  int64_t capacity() const { return static_cast<int64_t>(ring.size()); }
+  int32_t pop_free() {
+    const int32_t b = ring[static_cast<size_t>(head)];
+    head = head + 1 == capacity() ? 0 : head + 1;
+    --free_count;
+    return b;
+  }
+  // a block whose count reached 0 (at most num_blocks are ever queued)
+  void push_free(int32_t b) {
+    int64_t tail = head + free_count;
+    if (tail >= capacity()) tail -= capacity();
+    ring[static_cast<size_t>(tail)] = b;
+    ++free_count;
+  }
 };
 
 namespace {
@@ -54,10 +75,17 @@ int32_t pa_bm_create(int64_t num_blocks, int32_t block_size, pa_block_manager** 
   if (num_blocks < 1 || num_blocks > std::numeric_limits<int32_t>::max())
     return PA_ERR_INVALID_ARGUMENT;
   pa_block_manager* bm = new (std::nothrow) pa_block_manager();
-  if (!bm) return PA_ERR_INVALID_ARGUMENT;
+  if (!bm) return PA_ERR_HOST_MEMORY;
+  try {
+    bm->refcount.assign(static_cast<size_t>(num_blocks), 0);
+    bm->ring.resize(static_cast<size_t>(num_blocks));
+  } catch (...) {
+    delete bm;
+    return PA_ERR_HOST_MEMORY;
+  }
   bm->block_size = block_size;
-  bm->refcount.assign(static_cast<size_t>(num_blocks), 0);
-  for (int64_t b = 0; b < num_blocks; ++b) bm->free_queue.push_back(static_cast<int32_t>(b));
+  for (int64_t b = 0; b < num_blocks; ++b) bm->ring[static_cast<size_t>(b)] = static_cast<int32_t>(b);
+  bm->free_count = num_blocks;
   *out = bm;
   return PA_OK;
 }
@@ -65,7 +93,7 @@ int32_t pa_bm_create(int64_t num_blocks, int32_t block_size, pa_block_manager** 
 void pa_bm_destroy(pa_block_manager* bm) { delete bm; }
 
 int64_t pa_bm_num_free_blocks(const pa_block_manager* bm) {
-  return bm ? static_cast<int64_t>(bm->free_queue.size()) : -1;
+  return bm ? bm->free_count : -1;
 }
 
 int32_t pa_bm_allocate_slots(pa_block_manager* bm, int64_t seq_id, int32_t num_new_tokens,
@@ -78,15 +106,21 @@ int32_t pa_bm_allocate_slots(pa_block_manager* bm, int64_t seq_id, int32_t num_n
   const int64_t after = tokens + num_new_tokens;
   if (after + num_lookahead_tokens > kMaxTokens) return PA_ERR_INVALID_ARGUMENT;
   const int64_t need = bm->blocks_for(after + num_lookahead_tokens) - have;
-  if (need > static_cast<int64_t>(bm->free_queue.size())) return PA_ERR_NO_FREE_BLOCKS;
-  pa_block_manager::Sequence& s = bm->seqs[seq_id];  // creates a new sequence
-  for (int64_t i = 0; i < need; ++i) {
-    const int32_t b = bm->free_queue.front();
-    bm->free_queue.pop_front();
-    bm->refcount[b] = 1;
-    s.blocks.push_back(b);
+  if (need > bm->free_count) return PA_ERR_NO_FREE_BLOCKS;
+  pa_block_manager::Sequence* s = nullptr;
+  try {
+    s = &bm->seqs[seq_id];  // creates a new sequence
+    if (need > 0) s->blocks.reserve(static_cast<size_t>(have + need));
+  } catch (...) {
+    if (!existing) bm->seqs.erase(seq_id);
+    return PA_ERR_HOST_MEMORY;
   }
-  s.tokens = after;
+  for (int64_t i = 0; i < need; ++i) {
+    const int32_t b = bm->pop_free();
+    bm->refcount[b] = 1;
+    s->blocks.push_back(b);  // within the reserved capacity
+  }
+  s->tokens = after;
   return PA_OK;
 }
 
@@ -113,11 +147,17 @@ int32_t pa_bm_share_prefix(pa_block_manager* bm, int64_t src_seq, int64_t dst_se
       num_tokens > src->tokens)
     return PA_ERR_INVALID_ARGUMENT;
   const int64_t full = num_tokens / bm->block_size;  // whole blocks only
-  std::vector<int32_t> shared(src->blocks.begin(), src->blocks.begin() + full);
-  for (const int32_t b : shared) ++bm->refcount[b];
-  pa_block_manager::Sequence& d = bm->seqs[dst_seq];
-  d.blocks = std::move(shared);
-  d.tokens = full * bm->block_size;
+  pa_block_manager::Sequence* d = nullptr;
+  try {
+    std::vector<int32_t> shared(src->blocks.begin(), src->blocks.begin() + full);
+    d = &bm->seqs[dst_seq];
+    d->blocks = std::move(shared);
+  } catch (...) {
+    bm->seqs.erase(dst_seq);
+    return PA_ERR_HOST_MEMORY;
+  }
+  for (const int32_t b : d->blocks) ++bm->refcount[b];
+  d->tokens = full * bm->block_size;
   return PA_OK;
 }
 
@@ -126,7 +166,7 @@ int32_t pa_bm_free_sequence(pa_block_manager* bm, int64_t seq_id) {
   const auto it = bm->seqs.find(seq_id);
   if (it == bm->seqs.end()) return PA_ERR_INVALID_ARGUMENT;
   for (const int32_t b : it->second.blocks)
-    if (--bm->refcount[b] == 0) bm->free_queue.push_back(b);
+    if (--bm->refcount[b] == 0) bm->push_free(b);
   bm->seqs.erase(it);
   return PA_OK;
 }

@@ -165,6 +165,51 @@ def test_error_cases():
     assert bm.refcount(-1) == -1 and bm.refcount(8) == -1
 
 
+_OOM_SCRIPT = r"""
+import resource, sys
+sys.path.insert(0, sys.argv[1])
+import paged_kv_cache_token_amd as pa
+
+def vm_bytes():
+    for line in open("/proc/self/status"):
+        if line.startswith("VmSize:"):
+            return int(line.split()[1]) * 1024
+
+def status_of(f):
+    try:
+        f()
+    except pa.PAError as e:
+        return e.status
+    return 0
+
+bm = pa.BlockManager(1 << 26)
+assert bm.allocate_slots(1, 100)
+free0 = bm.num_free_blocks
+# from here on, at most 64 MiB more address space
+resource.setrlimit(resource.RLIMIT_AS, (vm_bytes() + (64 << 20), resource.RLIM_INFINITY))
+big = ((1 << 26) - 64) * 16      # tokens whose block list needs ~256 MiB
+assert status_of(lambda: pa.BlockManager((1 << 31) - 1)) == pa.PA_ERR_HOST_MEMORY
+assert status_of(lambda: bm.allocate_slots(2, big)) == pa.PA_ERR_HOST_MEMORY   # a new sequence
+assert status_of(lambda: bm.info(2)) == 3                                        # not created
+assert status_of(lambda: bm.allocate_slots(1, big)) == pa.PA_ERR_HOST_MEMORY   # a longer list
+assert bm.info(1) == (100, 7) and bm.num_free_blocks == free0                    # nothing changed
+assert bm.allocate_slots(3, 40) and bm.info(3) == (40, 3)                        # still usable
+print("ok")
+"""
+
+
+def test_host_allocation_failure_changes_nothing():
+    """Under an address-space limit (a child process), creating a huge manager
+    and growing a block list fail with PA_ERR_HOST_MEMORY instead of letting
+    a C++ exception out, and the manager is left as it was."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _OOM_SCRIPT, root], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
+
+
 class Model:
     """Brute-force model of the documented rules."""
 

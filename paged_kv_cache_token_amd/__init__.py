@@ -130,6 +130,19 @@ def _need(t: torch.Tensor, name: str, dtype=None, ndim=None):
         raise ValueError(f"{name} must have {ndim} dims")
 
 
+def _need_shape(t: torch.Tensor, name: str, shape: tuple):
+    """t has exactly `shape`: the kernels index every array by the counts the
+    call passes, so a shorter array would be read or written past its end."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _same_device(*ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"all tensors must be on one device, got {sorted(map(str, devs))}")
+
+
 def _check(call: str, status: int):
     if status != 0:
         raise PAError(call, status)
@@ -163,6 +176,12 @@ def build_slot_mapping(cu_seqlens: torch.Tensor, context_offsets: torch.Tensor,
         out = torch.empty(num_tokens, dtype=torch.int64, device=cu_seqlens.device)
     _need(out, "out", torch.int64, 1)
     n = context_offsets.shape[0]
+    _need_shape(cu_seqlens, "cu_seqlens", (n + 1,))
+    if block_tables.shape[0] != n:
+        raise ValueError(f"block_tables must have {n} rows, got {block_tables.shape[0]}")
+    if out.shape[0] < num_tokens:
+        raise ValueError(f"out holds {out.shape[0]} slots, fewer than num_tokens = {num_tokens}")
+    _same_device(cu_seqlens, context_offsets, block_tables, out)
     _check("pa_build_slot_mapping", lib.pa_build_slot_mapping(
         _ptr(out), _ptr(cu_seqlens), _ptr(context_offsets), _ptr(block_tables), n, num_tokens,
         block_tables.shape[1], BLOCK_SIZE, _stream(cu_seqlens)))
@@ -182,9 +201,20 @@ def write_kv(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor,
         raise ValueError("key/value must be [num_tokens, num_kv_heads, head_dim]")
     if v_cache.shape != k_cache.shape or slot_mapping.shape[0] != key.shape[0]:
         raise ValueError("cache shapes or slot_mapping length mismatch")
+    _same_device(key, value, k_cache, v_cache, slot_mapping)
     _check("pa_write_kv", lib.pa_write_kv(
         _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), key.shape[0],
         hkv, d, bs, num_blocks, _DTYPES[key.dtype], _stream(key)))
+
+
+def _decode_shapes(q, out, k_cache, v_cache, block_tables, context_lens, workspace, *extra):
+    n = q.shape[0]
+    _need_shape(out, "out", tuple(q.shape))
+    _need_shape(v_cache, "v_cache", tuple(k_cache.shape))
+    _need_shape(context_lens, "context_lens", (n,))
+    if block_tables.shape[0] != n:
+        raise ValueError(f"block_tables must have {n} rows, got {block_tables.shape[0]}")
+    _same_device(q, out, k_cache, v_cache, block_tables, context_lens, workspace, *extra)
 
 
 def decode_workspace_size(num_seqs: int, num_q_heads: int, head_dim: int, max_context_len: int,
@@ -209,6 +239,7 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     if out is None:
         out = torch.empty_like(q)
     _need(out, "out", q.dtype)
+    _decode_shapes(q, out, k_cache, v_cache, block_tables, context_lens, workspace)
     scale = float(d ** -0.5 if scale is None else scale)
     size = decode_workspace_size(n, hq, d, max_context_len, q.dtype)
     workspace, ws_bytes = _workspace(size, q, workspace)
@@ -240,6 +271,7 @@ def decode_step(q: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
     if out is None:
         out = torch.empty_like(q)
     _need(out, "out", q.dtype)
+    _decode_shapes(q, out, k_cache, v_cache, block_tables, context_lens, workspace, key, value)
     scale = float(d ** -0.5 if scale is None else scale)
     size = decode_workspace_size(n, hq, d, max_context_len, q.dtype)
     workspace, ws_bytes = _workspace(size, q, workspace)
@@ -277,6 +309,7 @@ def cascade_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     if out is None:
         out = torch.empty_like(q)
     _need(out, "out", q.dtype)
+    _decode_shapes(q, out, k_cache, v_cache, block_tables, context_lens, workspace)
     scale = float(d ** -0.5 if scale is None else scale)
     size = cascade_workspace_size(n, hq, hkv, d, max_context_len, num_common_prefix_blocks,
                                   q.dtype)
@@ -315,6 +348,12 @@ def varlen_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     if out is None:
         out = torch.empty_like(q)
     _need(out, "out", q.dtype)
+    _need_shape(out, "out", tuple(q.shape))
+    _need_shape(v_cache, "v_cache", tuple(k_cache.shape))
+    _need_shape(cu_seqlens, "cu_seqlens", (n + 1,))
+    if block_tables.shape[0] != n:
+        raise ValueError(f"block_tables must have {n} rows, got {block_tables.shape[0]}")
+    _same_device(q, out, k_cache, v_cache, cu_seqlens, context_offsets, block_tables, workspace)
     scale = float(d ** -0.5 if scale is None else scale)
     size = varlen_workspace_size(n, total_q, hq, hkv, d, max_context_len, q.dtype)
     workspace, ws_bytes = _workspace(size, q, workspace)

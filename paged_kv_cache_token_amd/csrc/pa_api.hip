@@ -64,6 +64,20 @@ int cascade_split_tiles(int num_seqs, int num_kv_heads, int group, int prefix_to
   }
   return std::min(st, std::max(tiles, 1));
 }
+// The private rest of every context in one partition (one item per
+// (sequence, kv head), on the single-partition kernel with its streaming
+// loads) when it fits one item and the pairs alone give the chip enough
+// items.  Measured with a 4096-token common prompt and private parts of
+// U[16, 1024] tokens: 128 sequences (1024 pairs) 96 us against 101 split
+// into 512-token partitions, 256 sequences 147 against 167; at 512 pairs
+// and fewer, splitting was faster (64 sequences 67 against 72).
+// PA_CASCADE_DIRECT=0/1 forces it off/on (if the rest fits one item).
+bool cascade_single_rest(int num_seqs, int num_kv_heads, int rest, int waves) {
+  if (rest <= 0 || rest > PA_BLOCK_SIZE * kMaxEntriesPerWave * waves) return false;
+  const char* e = getenv("PA_CASCADE_DIRECT");
+  if (e && *e) return atoi(e) != 0;
+  return (int64_t)num_seqs * num_kv_heads >= 1024;
+}
 // Partial slots per (seq, q head): the prefix splits (at most one per tile),
 // then the partitions of the rest of the longest context.
 int cascade_max_parts(int32_t max_context_len, int32_t prefix_blocks, int part_tokens,
@@ -328,6 +342,9 @@ int32_t pa_cascade_decode(void* out, const void* q, const void* k_cache, const v
                 &a.grid_mode, &a.oversub);
   a.key_start = prefix_tokens;
   a.prefix_parts = splits;
+  if (cascade_single_rest(num_seqs, num_kv_heads, max_context_len - prefix_tokens, a.waves))
+    a.part_tokens = std::max(a.part_tokens, ceil_div(max_context_len - prefix_tokens, PA_BLOCK_SIZE) *
+                                                PA_BLOCK_SIZE);
   a.max_parts = cascade_max_parts(max_context_len, num_common_prefix_blocks, a.part_tokens, splits);
   a.ws = decode_ws_layout(workspace, num_seqs, num_q_heads, head_dim, a.max_parts);
 

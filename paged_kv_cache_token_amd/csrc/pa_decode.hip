@@ -832,9 +832,15 @@ static int device_cus() {
 template <bool BF16, int D, int G, bool VARLEN, int NB>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   const dim3 block(64 * a.waves);
-  if (a.max_parts <= 1) {
+  if (a.max_parts - a.prefix_parts <= 1) {
+    // one partition per context (or per private part of a cascade decode,
+    // whose partials the merge then combines with the prefix's)
     hipLaunchKernelGGL((decode_direct_kernel<BF16, D, G, VARLEN, NB>),
                        dim3((unsigned)a.num_seqs * a.num_kv_heads), block, 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.prefix_parts == 0) return e;
+    hipLaunchKernelGGL((decode_merge_kernel<BF16, D, VARLEN>),
+                       dim3((unsigned)a.num_q_heads * a.num_seqs), dim3(D), 0, stream, a);
     return hipGetLastError();
   }
   hipError_t err;

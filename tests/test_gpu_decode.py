@@ -319,6 +319,18 @@ def test_decode_many_short_contexts(gpu, n, max_len):
     _check_decode(batch, seqs=seqs, check_pools=False)
 
 
+@pytest.mark.parametrize("dtype,d,hq,hkv,n", [("bf16", 128, 32, 8, 160), ("f32", 64, 8, 8, 130)])
+def test_decode_one_partition_up_to_1024(gpu, dtype, d, hq, hkv, n):
+    """At least 1024 (sequence, kv head) pairs with contexts of at most 1024
+    tokens run one partition per context on the streaming kernel (a context
+    of 1024 tokens in one item, no merge): every row against the oracle."""
+    rng = np.random.default_rng(39 + n)
+    lens = rng.integers(1, 1025, size=n)
+    lens[:6] = [1024, 1023, 513, 512, 511, 1]
+    batch = W.decode_batch(f"one_part_{dtype}_{n}", 39, lens, hq, hkv, d, dtype, pool_factor=1.2)
+    _check_decode(batch, check_pools=False)
+
+
 def test_decode_list_beyond_inline_plan(gpu):
     """More sequences than a workgroup derives its work list for (2048), with
     a context long enough to need partitions: the plan-kernel path."""

@@ -22,9 +22,12 @@ def _dev(a: np.ndarray, device) -> torch.Tensor:
 
 
 class DeviceBatch:
-    def __init__(self, batch: PagedBatch, device="cuda", fill: bool = True):
+    def __init__(self, batch: PagedBatch, device="cuda", fill: bool = True,
+                 hint_rows: bool = True):
         self.b = batch
         self.device = torch.device(device)
+        self.hint_rows = hint_rows
+        self.num_decode_rows = int((batch.q_lens == 1).sum()) if batch.num_seqs else 0
         self.block_tables = _dev(batch.block_tables, device)
         self.cu_seqlens = _dev(batch.cu_seqlens, device)
         self.context_offsets = _dev(batch.context_offsets, device)
@@ -74,9 +77,12 @@ class DeviceBatch:
             return pa.decode(self.q, self.k_cache, self.v_cache, self.block_tables,
                              self.context_lens, b.max_context_len, b.scale, out=out,
                              workspace=self.workspace)
+        # the host knows how many sequences are single-token rows (a step's
+        # metadata is built there): a prefill-only step launches no decode kernels
         return pa.varlen_prefill(self.q, self.k_cache, self.v_cache, self.cu_seqlens,
                                  self.context_offsets, self.block_tables, b.max_q_len,
-                                 b.max_context_len, b.scale, out=out, workspace=self.workspace)
+                                 b.max_context_len, b.scale, out=out, workspace=self.workspace,
+                                 num_decode_rows=self.num_decode_rows if self.hint_rows else None)
 
     def step(self) -> torch.Tensor:
         """One pass of the hot path: slots + write of the new tokens, attention

@@ -274,6 +274,32 @@ int32_t pa_varlen_prefill(void* out, const void* q, const void* k_cache, const v
                           int32_t dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_varlen_prefill_ex -- pa_varlen_prefill with the host's count of the
+ * step's single-token rows ([VI] forward-pass paragraph: the runner builds
+ * the step's attention metadata on the host, where it knows how many of the
+ * packed sequences are decode rows).
+ *
+ *   num_decode_rows  host count of sequences with exactly one query row, or
+ *                    any negative value for "unknown" (then the call is
+ *                    pa_varlen_prefill).  With 0 the call launches no decode
+ *                    kernels (a prefill-only step saves their launches); a
+ *                    positive count runs them as pa_varlen_prefill does.
+ *
+ * A count of 0 while some sequence has exactly one query row leaves that
+ * row of `out` unwritten (nothing is read or written out of bounds).
+ * Arguments, workspace (pa_varlen_workspace_size) and errors otherwise as
+ * pa_varlen_prefill; the output is bit-identical to it.
+ */
+int32_t pa_varlen_prefill_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* cu_seqlens, const int32_t* context_offsets,
+                             const int32_t* block_tables, int32_t num_seqs,
+                             int32_t total_q_tokens, int32_t max_q_len, int32_t max_context_len,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                             float scale, int32_t dtype, int32_t num_decode_rows,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_swap_blocks -- copy whole blocks between two block pools of one layout
  * ([KW] §2.2: the block manager moves inactive blocks out to host memory
  * when device memory runs short and back in when they are needed; the same

@@ -48,6 +48,9 @@ _SIGNATURES = {
     "pa_varlen_prefill": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32,
                                    _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                    _c_i64, _c_f32, _c_i32, _c_p, _c_sz, _c_p]),
+    "pa_varlen_prefill_ex": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32,
+                                      _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                      _c_i64, _c_f32, _c_i32, _c_i32, _c_p, _c_sz, _c_p]),
     "pa_swap_blocks": (_c_i32, [_c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_i64, _c_p]),
     # host-side block manager (include/pa_blocks.h)
     "pa_bm_create": (_c_i32, [_c_i64, _c_i32, ctypes.POINTER(_c_p)]),
@@ -333,8 +336,11 @@ def varlen_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                    cu_seqlens: torch.Tensor, context_offsets: torch.Tensor,
                    block_tables: torch.Tensor, max_q_len: int, max_context_len: int,
                    scale: float | None = None, out: torch.Tensor | None = None,
-                   workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """Packed super-sequence attention (pa_varlen_prefill); out [total_q, Hq, d]."""
+                   workspace: torch.Tensor | None = None,
+                   num_decode_rows: int | None = None) -> torch.Tensor:
+    """Packed super-sequence attention (pa_varlen_prefill); out [total_q, Hq, d].
+    ``num_decode_rows``: the host's count of single-token sequences
+    (pa_varlen_prefill_ex; 0 launches no decode kernels), None if unknown."""
     for t, nm in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _need(t, nm)
     _need(cu_seqlens, "cu_seqlens", torch.int32, 1)
@@ -357,11 +363,18 @@ def varlen_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     scale = float(d ** -0.5 if scale is None else scale)
     size = varlen_workspace_size(n, total_q, hq, hkv, d, max_context_len, q.dtype)
     workspace, ws_bytes = _workspace(size, q, workspace)
-    _check("pa_varlen_prefill", lib.pa_varlen_prefill(
-        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens), _ptr(context_offsets),
-        _ptr(block_tables), n, total_q, int(max_q_len), int(max_context_len), hq, hkv, d, bs,
-        block_tables.shape[1], num_blocks, scale, _DTYPES[q.dtype], _ptr(workspace), ws_bytes,
-        _stream(q)))
+    if num_decode_rows is None:
+        _check("pa_varlen_prefill", lib.pa_varlen_prefill(
+            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens),
+            _ptr(context_offsets), _ptr(block_tables), n, total_q, int(max_q_len),
+            int(max_context_len), hq, hkv, d, bs, block_tables.shape[1], num_blocks, scale,
+            _DTYPES[q.dtype], _ptr(workspace), ws_bytes, _stream(q)))
+    else:
+        _check("pa_varlen_prefill_ex", lib.pa_varlen_prefill_ex(
+            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cu_seqlens),
+            _ptr(context_offsets), _ptr(block_tables), n, total_q, int(max_q_len),
+            int(max_context_len), hq, hkv, d, bs, block_tables.shape[1], num_blocks, scale,
+            _DTYPES[q.dtype], int(num_decode_rows), _ptr(workspace), ws_bytes, _stream(q)))
     return out
 
 

@@ -394,6 +394,20 @@ int32_t pa_varlen_prefill(void* out, const void* q, const void* k_cache, const v
                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                           int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
                           int32_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return pa_varlen_prefill_ex(out, q, k_cache, v_cache, cu_seqlens, context_offsets,
+                              block_tables, num_seqs, total_q_tokens, max_q_len, max_context_len,
+                              num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                              num_blocks, scale, dtype, -1, workspace, workspace_bytes, stream);
+}
+
+int32_t pa_varlen_prefill_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* cu_seqlens, const int32_t* context_offsets,
+                             const int32_t* block_tables, int32_t num_seqs,
+                             int32_t total_q_tokens, int32_t max_q_len, int32_t max_context_len,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                             float scale, int32_t dtype, int32_t num_decode_rows,
+                             void* workspace, size_t workspace_bytes, void* stream) {
   if (!dtype_ok(dtype) || !head_dim_ok(head_dim) || block_size != PA_BLOCK_SIZE ||
       !heads_ok(num_q_heads, num_kv_heads))
     return PA_ERR_UNSUPPORTED;
@@ -473,8 +487,10 @@ int32_t pa_varlen_prefill(void* out, const void* q, const void* k_cache, const v
                 &a.grid_mode, &a.oversub);
   a.max_parts = decode_max_parts(max_context_len, a.part_tokens);
   if (a.max_parts > 1) a.ws = decode_ws_layout(ws, num_seqs, num_q_heads, head_dim, a.max_parts);
-  hipError_t err = launch_decode(a, s);
-  if (err != hipSuccess) return PA_ERR_HIP;
+  if (num_decode_rows != 0) {
+    const hipError_t err = launch_decode(a, s);
+    if (err != hipSuccess) return PA_ERR_HIP;
+  }
   if (max_q_len <= 1) return PA_OK;
 
   // multi-token chunks: the matrix-core prefill kernel

@@ -93,10 +93,16 @@ def test_slot_mapping_host_errors():
     assert s(None, None, None, None, 0, 0, 8, 16, None) == 0
 
 
-def test_varlen_host_errors():
+@pytest.mark.parametrize("rows", [None, -1, 0, 3])
+def test_varlen_host_errors(rows):
+    """pa_varlen_prefill and pa_varlen_prefill_ex (any single-row count)
+    refuse the same host-visible faults before launching anything."""
     def call(dtype=pa.PA_BF16, d=128, ws=FAKE, wsb=1 << 30, q=FAKE, n=4, total=40, maxq=20):
-        return L.pa_varlen_prefill(FAKE, q, FAKE, FAKE, FAKE, FAKE, FAKE, n, total, maxq, 600,
-                                   32, 8, d, 16, 64, 1000, 0.1, dtype, ws, wsb, None)
+        if rows is None:
+            return L.pa_varlen_prefill(FAKE, q, FAKE, FAKE, FAKE, FAKE, FAKE, n, total, maxq, 600,
+                                       32, 8, d, 16, 64, 1000, 0.1, dtype, ws, wsb, None)
+        return L.pa_varlen_prefill_ex(FAKE, q, FAKE, FAKE, FAKE, FAKE, FAKE, n, total, maxq, 600,
+                                      32, 8, d, 16, 64, 1000, 0.1, dtype, rows, ws, wsb, None)
     assert call(dtype=7) == 2
     assert call(d=80) == 2
     assert call(dtype=pa.PA_F32, q=None) == 1   # fp32 is supported: the pointer check decides

@@ -222,3 +222,45 @@ def test_packed_call_more_rows_than_grid_y(gpu):
     batch = W.varlen_batch("rows_70000", 25, np.ones(n, dtype=np.int64), ctx, 8, 1, 128, "bf16")
     seqs = sorted(set([0, 123, n - 1] + rng.choice(n, size=30, replace=False).tolist()))
     _check(batch, seqs=seqs)
+
+
+@pytest.mark.parametrize("name", ["prefill_only", "mixed"])
+def test_decode_row_count_hint(gpu, name):
+    """pa_varlen_prefill_ex with the host's count of single-token rows gives
+    pa_varlen_prefill's output bit for bit (0 for a prefill-only step, where
+    it launches no decode kernels)."""
+    from device_batch import DeviceBatch
+    if name == "prefill_only":
+        batch = W.varlen_batch("hint_chunks", 61, [70, 300, 2, 129], [0, 900, 5, 40], 32, 8, 128,
+                               "bf16")
+    else:
+        batch = W.varlen_batch("hint_mixed", 62, [1, 70, 1, 1, 200], [800, 30, 2000, 0, 0], 32,
+                               8, 128, "bf16")
+    a = DeviceBatch(batch, hint_rows=False)
+    want = a.step().clone()
+    b = DeviceBatch(batch, hint_rows=True)
+    say(name, "decode rows", b.num_decode_rows)
+    got = b.step().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
+
+
+def test_zero_row_count_skips_decode_rows(gpu):
+    """A count of 0 with single-token rows present: those rows of out are
+    left as they were, every chunk row is pa_varlen_prefill's."""
+    import paged_kv_cache_token_amd as pa
+    from device_batch import DeviceBatch
+    batch = W.varlen_batch("hint_zero", 63, [1, 90, 1, 40], [300, 10, 700, 0], 32, 8, 128, "bf16")
+    db = DeviceBatch(batch, hint_rows=False)
+    want = db.step().clone()
+    out = torch.full_like(want, 7.0)
+    pa.varlen_prefill(db.q, db.k_cache, db.v_cache, db.cu_seqlens, db.context_offsets,
+                      db.block_tables, batch.max_q_len, batch.max_context_len, batch.scale,
+                      out=out, workspace=db.workspace, num_decode_rows=0)
+    torch.cuda.synchronize()
+    ql = torch.as_tensor(batch.q_lens).long()
+    rows = (ql == 1).repeat_interleave(ql)
+    rows = rows.to(out.device)
+    assert (out[rows] == 7.0).all()
+    assert torch.equal(out[~rows], want[~rows])
+

@@ -44,7 +44,9 @@
 //     writes it instead past 2048 sequences);
 //   * a cascade decode's common prefix arrives as partials written by the
 //     matrix-core pass: the partitions start after it (key_start) and their
-//     slots follow its slots (prefix_parts), so the merge combines all.
+//     slots follow its slots (prefix_parts), so the merge combines all; when
+//     every private rest fits one partition, the (sequence, kv head) grid
+//     writes its one partial per pair and the merge follows it.
 // The order of every sum depends only on logical token positions, never on the
 // physical block ids, so the output is
 // bit-identical under any placement or sharing of blocks and between runs.

@@ -16,8 +16,11 @@
 
 namespace pa {
 
-// One workgroup per sequence; lanes walk that sequence's new tokens.  Token
-// indices outside [0, num_tokens) (inconsistent cu_seqlens) are not written.
+// Workgroups (sequence, y): lanes walk that sequence's new tokens, the
+// gridDim.y workgroups of a sequence interleaved in steps of 256 tokens, so a
+// long chunk's table lookups do not queue behind each other in one
+// workgroup.  Token indices outside [0, num_tokens) (inconsistent
+// cu_seqlens) are not written.
 __global__ __launch_bounds__(256) void slot_mapping_kernel(
     int64_t* __restrict__ slot_mapping, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ context_offsets, const int32_t* __restrict__ block_tables,
@@ -27,7 +30,8 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(
   const int hi = (int)min((int64_t)cu_seqlens[seq + 1], num_tokens);
   const int base = context_offsets[seq];
   const int32_t* table = block_tables + (int64_t)seq * max_blocks_per_seq;
-  for (int t = lo + (int)threadIdx.x; t < hi; t += blockDim.x) {
+  for (int t = lo + (int)(blockIdx.y * blockDim.x + threadIdx.x); t < hi;
+       t += blockDim.x * gridDim.y) {
     if (t < 0) continue;
     const int pos = base + (t - lo);
     const int logical = pos / kBlockSize;
@@ -66,7 +70,11 @@ hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* cu_seqlens,
                                int32_t num_seqs, int32_t max_blocks_per_seq, int64_t num_tokens,
                                hipStream_t stream) {
   if (num_seqs == 0) return hipSuccess;
-  hipLaunchKernelGGL(slot_mapping_kernel, dim3(num_seqs), dim3(256), 0, stream, slot_mapping,
+  // enough workgroups per sequence for one step over a chunk that holds every
+  // token, but at most ~4096 workgroups in all
+  const int64_t per_seq = (num_tokens + 255) / 256;
+  const int gy = (int)std::max<int64_t>(1, std::min<int64_t>(per_seq, 4096 / num_seqs));
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3(num_seqs, gy), dim3(256), 0, stream, slot_mapping,
                      cu_seqlens, context_offsets, block_tables, max_blocks_per_seq, num_tokens);
   return hipGetLastError();
 }

@@ -286,9 +286,11 @@ int32_t pa_varlen_prefill(void* out, const void* q, const void* k_cache, const v
  *                    positive count runs them as pa_varlen_prefill does.
  *
  * A count of 0 while some sequence has exactly one query row leaves that
- * row of `out` unwritten (nothing is read or written out of bounds).
+ * row of `out` unwritten on the matrix-core path (PA_BF16, head_dim 128;
+ * nothing is read or written out of bounds); the other types and head dims
+ * take every row through the decode kernels and ignore the count.
  * Arguments, workspace (pa_varlen_workspace_size) and errors otherwise as
- * pa_varlen_prefill; the output is bit-identical to it.
+ * pa_varlen_prefill; with a true count the output is bit-identical to it.
  */
 int32_t pa_varlen_prefill_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* cu_seqlens, const int32_t* context_offsets,

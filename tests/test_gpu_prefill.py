@@ -224,18 +224,20 @@ def test_packed_call_more_rows_than_grid_y(gpu):
     _check(batch, seqs=seqs)
 
 
-@pytest.mark.parametrize("name", ["prefill_only", "mixed"])
+@pytest.mark.parametrize("name", ["prefill_only", "mixed", "mixed_f32_rows"])
 def test_decode_row_count_hint(gpu, name):
     """pa_varlen_prefill_ex with the host's count of single-token rows gives
     pa_varlen_prefill's output bit for bit (0 for a prefill-only step, where
-    it launches no decode kernels)."""
+    it launches no decode kernels; the fp32 row path ignores the count)."""
     from device_batch import DeviceBatch
     if name == "prefill_only":
         batch = W.varlen_batch("hint_chunks", 61, [70, 300, 2, 129], [0, 900, 5, 40], 32, 8, 128,
                                "bf16")
-    else:
+    elif name == "mixed":
         batch = W.varlen_batch("hint_mixed", 62, [1, 70, 1, 1, 200], [800, 30, 2000, 0, 0], 32,
                                8, 128, "bf16")
+    else:
+        batch = W.varlen_batch("hint_f32", 64, [1, 33, 1, 9], [300, 20, 700, 0], 8, 2, 64, "f32")
     a = DeviceBatch(batch, hint_rows=False)
     want = a.step().clone()
     b = DeviceBatch(batch, hint_rows=True)

@@ -16,6 +16,12 @@
 
 namespace pa {
 
+// a 16-byte piece read with the non-temporal hint
+__device__ __forceinline__ uint4 load_once(const uint4* p) {
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+}
+
 // Workgroups (sequence, y): lanes walk that sequence's new tokens, the
 // gridDim.y workgroups of a sequence interleaved in steps of 256 tokens, so a
 // long chunk's table lookups do not queue behind each other in one
@@ -130,7 +136,11 @@ hipError_t launch_varlen_rows(int32_t* row_seq, int32_t* row_ctx, const int32_t*
 
 // Whole-block copies between two pools (swap out / in, or inside one pool):
 // one thread per 16-byte piece (grid-stride); consecutive lanes take
-// consecutive pieces of one block, so both sides move contiguous runs.
+// consecutive pieces of one block, so both sides move contiguous runs.  The
+// source is read with the non-temporal hint (each piece is read once): a
+// copy of 1024 random blocks inside a LLaMA-2-shaped pool measured 15%
+// faster that way; the same hint on the stores, or on the KV write's
+// source, gained nothing.
 __global__ __launch_bounds__(256) void swap_blocks_kernel(uint4* __restrict__ dst,
                                                           const uint4* __restrict__ src,
                                                           const int64_t* __restrict__ pairs,
@@ -143,7 +153,7 @@ __global__ __launch_bounds__(256) void swap_blocks_kernel(uint4* __restrict__ ds
     const int64_t piece = idx - p * pieces;
     const int64_t s = pairs[2 * p], d = pairs[2 * p + 1];
     if (s < 0 || s >= src_blocks || d < 0 || d >= dst_blocks) continue;
-    dst[d * pieces + piece] = src[s * pieces + piece];
+    dst[d * pieces + piece] = load_once(src + s * pieces + piece);
   }
 }
 

@@ -14,7 +14,7 @@ Sources, cited by page title and section:
         paragraph (the model runner builds a slot mapping and attention
         metadata; all sequences are packed into one super-sequence whose masks
         and positions keep each sequence on its own tokens).
-  [VS]  "vLLMつかったら、ベクトル検索サーバーが高速化して安定性も向上した" --
+  [ZN]  "vLLMつかったら、ベクトル検索サーバーが高速化して安定性も向上した" --
         the walk through Scheduler.schedule() (its output carries the number
         of blocks common to every scheduled request).
   [KW]  "vLLM：颠覆大模型推理的高效API服务引擎深度解析" --
@@ -209,7 +209,7 @@ def cascade_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                    block_size: int = BLOCK_SIZE) -> np.ndarray:
     """Decode of sequences that share their first ``num_common_prefix_blocks``
     physical blocks (the scheduler's count of blocks common to every request,
-    [VS] Scheduler.schedule(); blocks referenced read-only by several block
+    [ZN] Scheduler.schedule(); blocks referenced read-only by several block
     tables, [KW] §1.3).
 
     Attending the common prefix once for all sequences and each private rest

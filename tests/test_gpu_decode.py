@@ -331,6 +331,16 @@ def test_decode_one_partition_up_to_1024(gpu, dtype, d, hq, hkv, n):
     _check_decode(batch, check_pools=False)
 
 
+@pytest.mark.parametrize("dtype,d,hq,hkv", [("bf16", 128, 32, 8), ("f32", 128, 8, 8)])
+def test_decode_very_long_context(gpu, dtype, d, hq, hkv):
+    """A 65536-token context next to short ones: 1024-token partitions (64 of
+    them, more than one batch of the merge's loads) and the fused step's
+    store at the far end of the table; every row against the oracle."""
+    lens = [65536, 1, 700, 65535 - 16 * 7]
+    batch = W.decode_batch(f"very_long_{dtype}", 40, lens, hq, hkv, d, dtype, pool_factor=1.05)
+    _check_decode(batch, check_pools=False)
+
+
 def test_decode_list_beyond_inline_plan(gpu):
     """More sequences than a workgroup derives its work list for (2048), with
     a context long enough to need partitions: the plan-kernel path."""

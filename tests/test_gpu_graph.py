@@ -88,3 +88,23 @@ def test_graph_cascade_decode(gpu):
         return db.cascade(out)
     _replays(lambda: W.shared_prefix_decode(seed=58, n=70, prefix_blocks=20,
                                             suffix_range=(1, 1500)), run)
+
+
+def test_graph_cascade_single_partition_rest(gpu):
+    # >= 1024 (sequence, kv head) pairs with short private parts: the prefix
+    # pass, the single-partition kernel writing one partial per pair, and the
+    # merge, captured together
+    def run(db, out=None):
+        db.write_new()
+        return db.cascade(out)
+    _replays(lambda: W.shared_prefix_decode(seed=59, n=130, prefix_blocks=20,
+                                            suffix_range=(1, 1500)), run)
+
+
+def test_graph_prefill_only_step(gpu):
+    # a packed step with no single-token rows, the row count passed: slot
+    # mapping, store, the prefill plan and the prefill kernel only
+    def run(db, out=None):
+        db.write_new()
+        return db.attend(out)
+    _replays(W.prefill_only, run)

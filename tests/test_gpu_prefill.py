@@ -245,6 +245,13 @@ def test_decode_row_count_hint(gpu, name):
     got = b.step().clone()
     torch.cuda.synchronize()
     assert torch.equal(got, want)
+    # "unknown" (negative) and a positive count that overstates the rows run
+    # the decode kernels as pa_varlen_prefill does: the same output
+    for count in (-1, b.num_decode_rows + 3):
+        b.num_decode_rows = count
+        again = b.attend().clone()
+        torch.cuda.synchronize()
+        assert torch.equal(again, want), count
 
 
 def test_zero_row_count_skips_decode_rows(gpu):

@@ -156,7 +156,7 @@ struct DecodeArgs {
   void* v_cache_w;
   DecodeWorkspace ws;              // valid when max_parts > 1
   int32_t max_parts;               // partitions of the longest context
-  int32_t part_tokens;             // split-K partition length (multiple of 16 * waves)
+  int32_t part_tokens;             // split-K partition length (a multiple of 16 tokens)
   int32_t waves;                   // waves per workgroup
   int32_t buffers;                 // K/V register buffers per wave (2..4)
   int32_t grid_mode;               // multi-partition: 1 = (seq, kvh, part) grid, 0 = work list

@@ -170,3 +170,15 @@ def test_cascade_full_shared_prefix_sampled(gpu):
     err = float((out.float() - dec.float()).abs().max())
     say("cascade vs decode max abs diff", err)
     assert err <= TOL["bf16"], err
+
+
+@pytest.mark.parametrize("direct", ["0", "1"])
+def test_cascade_private_parts_split_or_whole(gpu, monkeypatch, direct):
+    """>= 1024 (sequence, kv head) pairs whose private parts fit one item:
+    one partition per private part (the default) or 512-token partitions
+    (PA_CASCADE_DIRECT=0), both against the oracle."""
+    monkeypatch.setenv("PA_CASCADE_DIRECT", direct)
+    batch = W.shared_prefix_decode(seed=60, n=132, prefix_blocks=24, suffix_range=(1, 1800))
+    p = 24 * 16
+    seqs = sorted(set(list(range(6)) + [66, 131]))
+    _check(batch, ctx={0: 7, 1: p, 2: p + 1}, seqs=seqs)

@@ -3,6 +3,7 @@ dim, head ratio, sequence count, context lengths with partition and block
 edges mixed in, chunk lengths, pool slack, common-prefix length) through the
 decode, packed and cascade calls, each checked against the oracle: pools bit
 for bit, outputs within max-abs 1e-5 (fp32) / 2e-2 (bf16)."""
+import os
 import sys
 
 import numpy as np
@@ -17,6 +18,9 @@ from oracle_side import bits_equal, expected, host_state
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-5, "bf16": 2e-2}
+# cases per call kind; PA_TEST_SWEEP_CASES=N draws N of each (same generator,
+# the first cases unchanged) for a longer run
+N_CASES = int(os.environ.get("PA_TEST_SWEEP_CASES", "0")) or None
 # lengths that sit on the edges the kernels care about: one block, a tile of
 # 64 keys, a 512-token partition, a 1024-token partition
 EDGES = [1, 2, 15, 16, 17, 63, 64, 65, 255, 256, 257, 511, 512, 513, 1023, 1024, 1025]
@@ -86,7 +90,7 @@ def _max_err(got, want):
     return float(np.abs(g - want).max()) if want.size else 0.0
 
 
-@pytest.mark.parametrize("i", range(24))
+@pytest.mark.parametrize("i", range(N_CASES or 24))
 def test_sweep_decode(gpu, i):
     from device_batch import DeviceBatch
     b = _decode_case(i)
@@ -102,7 +106,7 @@ def test_sweep_decode(gpu, i):
     assert err <= TOL[b.dtype], err
 
 
-@pytest.mark.parametrize("i", range(24))
+@pytest.mark.parametrize("i", range(N_CASES or 24))
 def test_sweep_varlen(gpu, i):
     from device_batch import DeviceBatch
     b = _varlen_case(i)
@@ -121,7 +125,7 @@ def test_sweep_varlen(gpu, i):
     assert err <= TOL[b.dtype], err
 
 
-@pytest.mark.parametrize("i", range(16))
+@pytest.mark.parametrize("i", range(N_CASES or 16))
 def test_sweep_cascade(gpu, i):
     from device_batch import DeviceBatch
     b = _cascade_case(i)

@@ -77,7 +77,7 @@ typedef enum pa_status {
   PA_OK = 0,
   PA_ERR_NULL_POINTER = 1,        /* a required pointer is NULL */
   PA_ERR_UNSUPPORTED = 2,         /* dtype, head_dim, block_size or head ratio */
-  PA_ERR_INVALID_ARGUMENT = 3,    /* negative or inconsistent count */
+  PA_ERR_INVALID_ARGUMENT = 3,    /* negative or inconsistent count, non-finite scale */
   PA_ERR_WORKSPACE_TOO_SMALL = 4, /* workspace_bytes below the size query */
   PA_ERR_HIP = 5,                 /* the HIP runtime refused a launch */
   PA_ERR_NO_FREE_BLOCKS = 6,      /* block manager: the free queue is too short */
@@ -150,7 +150,10 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t h
  *   context_lens     in   int32 [num_seqs]: tokens in the cache for sequence i,
  *                         including this step's new token (write it first)
  *   max_context_len       host copy of max(context_lens) (sizes the grid)
- *   scale                 softmax scale, usually 1/sqrt(head_dim)
+ *   scale                 softmax scale, usually 1/sqrt(head_dim); any finite
+ *                         value (0 weighs every key alike, a negative one favours
+ *                         the smallest scores); NaN or an infinity is refused
+ *                         with PA_ERR_INVALID_ARGUMENT (every attention call)
  *   workspace             device scratch of >= pa_decode_workspace_size(...)
  *                         bytes (may be NULL when that size is 0)
  *
@@ -180,8 +183,13 @@ int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_c
  *                         workspace size from pa_decode_workspace_size)
  *
  * The new token's K/V take part in the attention from the inputs, so the
- * result does not depend on when the store becomes visible.  A sequence whose
- * slot block id is outside the pool gets no store.
+ * result does not depend on when the store becomes visible.  Its position is
+ * context_lens[i] - 1 as given, before any clamp to max_context_len or the
+ * table's size: it is stored into that position's slot whenever the
+ * position's block lies inside the table row and names a block of the pool
+ * (what pa_build_slot_mapping + pa_write_kv store), and it takes part in the
+ * attention only when the clamped context still includes it.  So an
+ * understated max_context_len never redirects the store onto an older token.
  */
 int32_t pa_decode_step(void* out, const void* q, const void* key, const void* value,
                        void* k_cache, void* v_cache, const int32_t* block_tables,

@@ -5,6 +5,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "../../include/pa.h"
 #include "pa_launch.h"
@@ -22,6 +23,25 @@ bool heads_ok(int32_t hq, int32_t hkv) {
   return g == 1 || g == 2 || g == 4 || g == 8;
 }
 int32_t from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+// a softmax scale the kernels can use: finite (NaN or an infinity would give
+// no defined weights)
+bool scale_ok(float scale) { return std::isfinite(scale); }
+
+// The matrix-core kernels fold a positive scale into their exponentials; any
+// finite scale reaches that form exactly: scale < 0 as (-q, |scale|), 0 as
+// (q = 0, 1), both giving the same scale * <q, k> for every key.
+void set_prefill_scale(PrefillArgs& p, float scale) {
+  if (scale > 0.f) {
+    p.scale = scale;
+    p.q_sign = 1;
+  } else if (scale < 0.f) {
+    p.scale = -scale;
+    p.q_sign = -1;
+  } else {
+    p.scale = 1.f;
+    p.q_sign = 0;
+  }
+}
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -87,6 +107,56 @@ int cascade_max_parts(int32_t max_context_len, int32_t prefix_blocks, int part_t
   return splits + decode_max_parts(std::max(max_context_len - prefix_tokens, 0), part_tokens);
 }
 
+
+// Host checks of a plain decode call (PA_OK: go on).
+int32_t decode_checks(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                      int32_t max_context_len, int64_t num_blocks, float scale, int32_t dtype) {
+  if (!dtype_ok(dtype) || !head_dim_ok(head_dim) || block_size != PA_BLOCK_SIZE ||
+      !heads_ok(num_q_heads, num_kv_heads))
+    return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || num_blocks <= 0 ||
+      !scale_ok(scale))
+    return PA_ERR_INVALID_ARGUMENT;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return PA_ERR_NULL_POINTER;
+  return PA_OK;
+}
+
+// A plain decode call's launch arguments and shape-based launch choice (the
+// workspace layout is the caller's to add when max_parts > 1).
+DecodeArgs decode_args(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens,
+                       int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t max_blocks_per_seq, int32_t max_context_len,
+                       int64_t num_blocks, float scale, int32_t dtype) {
+  DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.q_rows = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.num_blocks = num_blocks;
+  a.scale = scale;
+  a.dtype = dtype;
+  a.varlen = false;
+  decode_config(num_seqs, num_kv_heads, max_context_len, &a.waves, &a.part_tokens, &a.buffers,
+                &a.grid_mode, &a.oversub);
+  a.max_parts = decode_max_parts(max_context_len, a.part_tokens);
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -99,7 +169,8 @@ const char* pa_status_string(int32_t status) {
     case PA_ERR_NULL_POINTER: return "a required pointer is NULL";
     case PA_ERR_UNSUPPORTED:
       return "unsupported dtype, head_dim, block_size or query/kv head ratio";
-    case PA_ERR_INVALID_ARGUMENT: return "negative or inconsistent size argument";
+    case PA_ERR_INVALID_ARGUMENT:
+      return "negative or inconsistent size argument, or a non-finite softmax scale";
     case PA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than the size query returned";
     case PA_ERR_HIP: return "the HIP runtime rejected a kernel launch";
     case PA_ERR_NO_FREE_BLOCKS: return "not enough free blocks in the pool";
@@ -186,40 +257,17 @@ int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_c
                   int32_t block_size, int32_t max_blocks_per_seq, int32_t max_context_len,
                   int64_t num_blocks, float scale, int32_t dtype, void* workspace,
                   size_t workspace_bytes, void* stream) {
-  if (!dtype_ok(dtype) || !head_dim_ok(head_dim) || block_size != PA_BLOCK_SIZE ||
-      !heads_ok(num_q_heads, num_kv_heads))
-    return PA_ERR_UNSUPPORTED;
-  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || num_blocks <= 0)
-    return PA_ERR_INVALID_ARGUMENT;
-  if (num_seqs == 0) return PA_OK;
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
-    return PA_ERR_NULL_POINTER;
+  const int32_t st = decode_checks(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                                   num_q_heads, num_kv_heads, head_dim, block_size,
+                                   max_blocks_per_seq, max_context_len, num_blocks, scale, dtype);
+  if (st != PA_OK || num_seqs == 0) return st;
   const size_t need =
       pa_decode_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, dtype);
   if (workspace_bytes < need) return PA_ERR_WORKSPACE_TOO_SMALL;
   if (need > 0 && !workspace) return PA_ERR_NULL_POINTER;
-
-  DecodeArgs a{};
-  a.out = out;
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.num_seqs = num_seqs;
-  a.q_rows = num_seqs;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.head_dim = head_dim;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.max_context_len = max_context_len;
-  a.num_blocks = num_blocks;
-  a.scale = scale;
-  a.dtype = dtype;
-  a.varlen = false;
-  decode_config(num_seqs, num_kv_heads, max_context_len, &a.waves, &a.part_tokens, &a.buffers,
-                &a.grid_mode, &a.oversub);
-  a.max_parts = decode_max_parts(max_context_len, a.part_tokens);
+  DecodeArgs a = decode_args(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                             num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                             max_context_len, num_blocks, scale, dtype);
   if (a.max_parts > 1)
     a.ws = decode_ws_layout(workspace, num_seqs, num_q_heads, head_dim, a.max_parts);
   return from_hip(launch_decode(a, static_cast<hipStream_t>(stream)));
@@ -235,7 +283,8 @@ int32_t pa_decode_step(void* out, const void* q, const void* key, const void* va
   if (!dtype_ok(dtype) || !head_dim_ok(head_dim) || block_size != PA_BLOCK_SIZE ||
       !heads_ok(num_q_heads, num_kv_heads))
     return PA_ERR_UNSUPPORTED;
-  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || num_blocks <= 0)
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || num_blocks <= 0 ||
+      !scale_ok(scale))
     return PA_ERR_INVALID_ARGUMENT;
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !key || !value || !k_cache || !v_cache || !block_tables || !context_lens)
@@ -301,7 +350,8 @@ int32_t pa_cascade_decode(void* out, const void* q, const void* k_cache, const v
       !heads_ok(num_q_heads, num_kv_heads))
     return PA_ERR_UNSUPPORTED;
   if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || num_blocks <= 0 ||
-      num_common_prefix_blocks < 0 || num_common_prefix_blocks > max_blocks_per_seq)
+      num_common_prefix_blocks < 0 || num_common_prefix_blocks > max_blocks_per_seq ||
+      !scale_ok(scale))
     return PA_ERR_INVALID_ARGUMENT;
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
@@ -362,7 +412,7 @@ int32_t pa_cascade_decode(void* out, const void* q, const void* k_cache, const v
   p.max_blocks_per_seq = max_blocks_per_seq;
   p.max_context_len = max_context_len;
   p.num_blocks = num_blocks;
-  p.scale = scale;
+  set_prefill_scale(p, scale);
   p.part_ml = a.ws.ml;
   p.part_acc = a.ws.acc;
   p.max_parts = a.max_parts;
@@ -412,7 +462,7 @@ int32_t pa_varlen_prefill_ex(void* out, const void* q, const void* k_cache, cons
       !heads_ok(num_q_heads, num_kv_heads))
     return PA_ERR_UNSUPPORTED;
   if (num_seqs < 0 || total_q_tokens < 0 || max_q_len < 0 || max_context_len < 0 ||
-      max_blocks_per_seq <= 0 || num_blocks <= 0)
+      max_blocks_per_seq <= 0 || num_blocks <= 0 || !scale_ok(scale))
     return PA_ERR_INVALID_ARGUMENT;
   if (num_seqs == 0 || total_q_tokens == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !cu_seqlens || !context_offsets || !block_tables)
@@ -510,7 +560,7 @@ int32_t pa_varlen_prefill_ex(void* out, const void* q, const void* k_cache, cons
   p.max_blocks_per_seq = max_blocks_per_seq;
   p.max_context_len = max_context_len;
   p.num_blocks = num_blocks;
-  p.scale = scale;
+  set_prefill_scale(p, scale);
   p.work = reinterpret_cast<int32_t*>(ws + dec_bytes);
   p.work_cap =
       prefill_work_capacity(num_seqs, total_q_tokens, num_kv_heads, num_q_heads / num_kv_heads);

@@ -277,12 +277,19 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int seq, int pa
   const int nblk = tok1 > tok0 ? ceil_div(tok1 - tok0, kBlockSize) : 0;
   const int nmine = nblk > wave ? ceil_div(nblk - wave, nwaves) : 0;  // <= 64
 
-  // Fused step: the item holding position ctx-1 uses the new token's K/V from
-  // the inputs instead of re-reading the cache (no read-after-write within the
-  // launch), and stores them into their slot once its loads are issued.
-  const bool fused = a.key_new != nullptr && ctx > 0 && ctx - 1 >= tok0 && ctx - 1 < tok1;
-  const int new_off = (ctx - 1) % kBlockSize;                      // row inside its block
-  const int new_blk = fused ? (ctx - 1 - tok0) / kBlockSize : -1;  // partition-local block
+  // Fused step: the new token sits at position context_lens[seq] - 1, taken
+  // before any clamp (as the separate slot-mapping call takes it).  The item
+  // whose keys hold that position uses the new K/V from the inputs instead of
+  // re-reading the cache (no read-after-write within the launch) and stores
+  // them into their slot once its loads are issued.  When the declared maxima
+  // clamp the context below the position, no item attends it, and the item of
+  // the last partition stores it (its slot still comes from the table, as
+  // with the separate calls; past the table's end nothing is stored).
+  const int new_pos = a.key_new != nullptr ? a.context_lens[seq] - 1 : -1;
+  const bool fused = new_pos >= 0 && new_pos < ctx && new_pos >= tok0 && new_pos < tok1;
+  const bool store = fused || (new_pos >= ctx && part == nparts - 1);
+  const int new_off = new_pos % kBlockSize;                        // row inside its block
+  const int new_blk = fused ? (new_pos - tok0) / kBlockSize : -1;  // partition-local block
 
   float m[G], l[G], acc[G][EPL];
 #pragma unroll
@@ -482,8 +489,8 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int seq, int pa
     }
   }
 
-  if (fused && wave == 0 && lane < LPT) {
-    const int raw = a.block_tables[(int64_t)tseq * a.max_blocks_per_seq + (ctx - 1) / kBlockSize];
+  if (store && wave == 0 && lane < LPT && new_pos / kBlockSize < a.max_blocks_per_seq) {
+    const int raw = a.block_tables[(int64_t)tseq * a.max_blocks_per_seq + new_pos / kBlockSize];
     if (raw >= 0 && (int64_t)raw < a.num_blocks) {
       const int64_t dst = (((int64_t)raw * hkv + kvh) * kBlockSize + new_off) * LPT + lane;
       static_cast<uint4*>(a.k_cache_w)[dst] = knew;

@@ -186,7 +186,11 @@ struct PrefillArgs {
   int32_t max_blocks_per_seq;
   int32_t max_context_len;
   int64_t num_blocks;
-  float scale;
+  float scale;         // > 0: the kernels fold it into exp2 with a running max in raw
+                       // score units, which only orders scores correctly for scale > 0
+  int32_t q_sign;      // how the call's scale reaches that form: 1 = q as is (scale > 0),
+                       // -1 = q negated, scale = |call scale| (s * scale unchanged),
+                       // 0 = q zeroed, scale = 1 (every visible key weighs the same)
   int32_t* work;       // work list in the workspace
   int32_t work_cap;    // capacity in items
   // common-prefix pass of a decode call (the rows are the sequences' single

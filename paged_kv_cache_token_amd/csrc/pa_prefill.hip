@@ -314,10 +314,17 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const ItemMet
   {
     const uint4* qrow = static_cast<const uint4*>(a.q) +
                         ((int64_t)(valid_q ? lo_row + q0 + tok : 0) * hq + head) * (D / 8);
+    // a call with scale < 0 runs on -q and |scale| (negating a bf16 flips its
+    // sign bit: exact), one with scale 0 on q = 0 (all scores 0: uniform weights)
+    const uint32_t flip = a.q_sign < 0 ? 0x80008000u : 0u;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       uint4 v = qrow[ks * 2 + hi];
-      if (!valid_q) v = make_uint4(0u, 0u, 0u, 0u);
+      v.x ^= flip;
+      v.y ^= flip;
+      v.z ^= flip;
+      v.w ^= flip;
+      if (!valid_q || a.q_sign == 0) v = make_uint4(0u, 0u, 0u, 0u);
       qf[ks] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
@@ -454,8 +461,9 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const ItemMet
     e2 = entries(t + 3);
     const int bad = bq & 15;
     // cur[u][4i+j] is the raw score of key t*64 + 32u + 8i + 4hi + j for this
-    // row; the running max m is kept in raw units (scale > 0) and the scale
-    // is folded into the exponent: p = 2^(s*scale*log2e - m*scale*log2e)
+    // row; the running max m is kept in raw units (scale > 0 here: the host
+    // turns other scales into that form through q_sign) and the scale is
+    // folded into the exponent: p = 2^(s*scale*log2e - m*scale*log2e)
     const int kt0 = (tile0 + t) * kKeyTile;
     // every key of the tile visible to every row: no masking
     const bool full = bad == 0 && kt0 + kKeyTile <= full_lim;

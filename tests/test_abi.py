@@ -158,3 +158,20 @@ def test_swap_blocks_rejects_pageable_host_tensors():
     with pytest.raises(ValueError):
         pa.swap_blocks(torch.zeros(4, 2, 16, 8), torch.zeros(4, 2, 16, 8),
                        torch.zeros(1, 2, dtype=torch.int64))
+
+
+@pytest.mark.parametrize("scale", [float("nan"), float("inf"), -float("inf")])
+def test_attention_calls_refuse_non_finite_scale(scale):
+    """A NaN or infinite softmax scale defines no weights: every attention
+    call refuses it with PA_ERR_INVALID_ARGUMENT before launching anything
+    (any finite scale, zero and negative included, is taken)."""
+    assert _decode(scale=scale) == 3
+    assert L.pa_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 2, 128, 16, 8,
+                            100, 64, scale, pa.PA_BF16, None, 0, None) == 3
+    assert L.pa_cascade_decode(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 2, 128, 16, 8, 300, 64,
+                               4, scale, pa.PA_BF16, FAKE, 1 << 30, None) == 3
+    assert L.pa_varlen_prefill(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 40, 20, 600, 32, 8,
+                               128, 16, 64, 1000, scale, pa.PA_BF16, FAKE, 1 << 30, None) == 3
+    assert L.pa_varlen_prefill_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 40, 20, 600, 32,
+                                  8, 128, 16, 64, 1000, scale, pa.PA_BF16, 0, FAKE, 1 << 30,
+                                  None) == 3

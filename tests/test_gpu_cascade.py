@@ -182,3 +182,26 @@ def test_cascade_private_parts_split_or_whole(gpu, monkeypatch, direct):
     p = 24 * 16
     seqs = sorted(set(list(range(6)) + [66, 131]))
     _check(batch, ctx={0: 7, 1: p, 2: p + 1}, seqs=seqs)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.0883883476])
+def test_cascade_any_finite_scale(gpu, scale):
+    """The common-prefix pass runs on the matrix cores, which fold a positive
+    scale into their exponentials: a zero or negative scale still gives the
+    oracle's attention with that scale (prefix partials merged with the
+    decode kernels' private parts)."""
+    import paged_kv_cache_token_amd as pa
+    batch = W.shared_prefix_decode(seed=61, n=70, prefix_blocks=9, suffix_range=(1, 900))
+    say(batch.name, "scale", scale)
+    db = _device_batch(batch)
+    db.write_new()
+    p = batch.notes["prefix_tokens"] // 16
+    out = pa.cascade_decode(db.q, db.k_cache, db.v_cache, db.block_tables, db.context_lens,
+                            batch.max_context_len, p, scale)
+    torch.cuda.synchronize()
+    hs = host_state(batch)
+    want = oracle.cascade_decode(hs.q, hs.k_cache, hs.v_cache, batch.block_tables,
+                                 batch.context_lens, p, scale)
+    err = _max_err(out, want)
+    say("max abs err", err)
+    assert err <= TOL["bf16"], err

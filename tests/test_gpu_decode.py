@@ -205,6 +205,30 @@ def test_fused_step_equals_separate_calls(gpu, name):
     assert bits_equal(host_bits(a.v_cache), host_bits(b.v_cache))
 
 
+@pytest.mark.parametrize("max_ctx", [600, 1000])
+def test_fused_step_understated_max_context(gpu, max_ctx):
+    """With max_context_len below some contexts, the fused step still stores
+    each new token at position context_lens[i] - 1 (never over an older
+    token), and attends what pa_decode attends under the same clamp: pools
+    and output bit-identical to slot mapping + pa_write_kv + pa_decode."""
+    lens = [1, 17, 300, 599, 600, 601, 700, 1100, 1500]
+    batch = W.decode_batch("fused_clamp", 34, lens, 16, 4, 128, "bf16", pool_factor=1.3)
+    say("fused step, max_context_len", max_ctx, "of", batch.max_context_len)
+    import paged_kv_cache_token_amd as pa
+    a, b = _device_batch(batch), _device_batch(batch)
+    a.write_new()
+    oa = pa.decode(a.q, a.k_cache, a.v_cache, a.block_tables, a.context_lens, max_ctx,
+                   batch.scale).clone()
+    ob = pa.decode_step(b.q, b.k_new, b.v_new, b.k_cache, b.v_cache, b.block_tables,
+                        b.context_lens, max_ctx, batch.scale).clone()
+    torch.cuda.synchronize()
+    hs = host_state(batch)
+    assert bits_equal(host_bits(a.k_cache), hs.k_cache)
+    assert bits_equal(host_bits(b.k_cache), hs.k_cache), "fused store went to another slot"
+    assert bits_equal(host_bits(b.v_cache), hs.v_cache), "fused store went to another slot"
+    assert torch.equal(oa, ob)
+
+
 def test_fused_step_against_oracle(gpu):
     batch = W.decode_batch("fused_oracle", 33, [1, 16, 17, 700, 1500], 16, 4, 128, "bf16",
                            pool_factor=1.3)

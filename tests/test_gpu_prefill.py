@@ -273,3 +273,30 @@ def test_zero_row_count_skips_decode_rows(gpu):
     assert (out[rows] == 7.0).all()
     assert torch.equal(out[~rows], want[~rows])
 
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.0883883476, -1.0])
+def test_varlen_any_finite_scale(gpu, scale):
+    """The matrix-core path takes any finite scale, as the decode kernels do:
+    0 weighs every visible key alike, a negative scale favours the smallest
+    scores.  Chunks (matrix cores) and a decode row against the oracle run
+    with the same scale."""
+    import oracle
+    import paged_kv_cache_token_amd as pa
+    batch = W.varlen_batch("any_scale", 27, [90, 1, 33, 200], [70, 300, 0, 64], 32, 8, 128,
+                           "bf16")
+    say(batch.name, "scale", scale)
+    db = _device_batch(batch)
+    db.write_new()
+    out = pa.varlen_prefill(db.q, db.k_cache, db.v_cache, db.cu_seqlens, db.context_offsets,
+                            db.block_tables, batch.max_q_len, batch.max_context_len, scale)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    hs = host_state(batch)
+    want = oracle.varlen_prefill(hs.q, hs.k_cache, hs.v_cache, batch.cu_seqlens,
+                                 batch.context_offsets, batch.block_tables, scale)
+    err = max(float(np.abs(got[int(batch.cu_seqlens[i]):int(batch.cu_seqlens[i + 1])] - w).max())
+              for i, w in want.items())
+    say("max abs err", err)
+    assert err <= TOL, err

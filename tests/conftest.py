@@ -30,3 +30,26 @@ def gpu():
         pytest.skip("no GPU")
     import paged_kv_cache_token_amd as pa  # raises if the HIP library is missing
     return pa
+
+
+def route_block_manager(pa):
+    """When PA_TEST_BLOCKS_LIB names a host-only build of the block manager
+    (csrc/pa_blocks.cpp under the sanitizers), send the binding's pa_bm_*
+    calls to it; every other call keeps going to libpa.so."""
+    path = os.environ.get("PA_TEST_BLOCKS_LIB")
+    if not path:
+        return
+    import ctypes
+    san = ctypes.CDLL(path)
+    real = pa.lib
+
+    class Routed:
+        def __getattr__(self, name):
+            fn = getattr(real, name)
+            if not name.startswith("pa_bm_"):
+                return fn
+            alt = getattr(san, name)
+            alt.restype, alt.argtypes = fn.restype, fn.argtypes
+            return alt
+
+    pa.lib = Routed()

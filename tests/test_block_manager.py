@@ -15,7 +15,11 @@ import pytest
 
 import oracle
 import paged_kv_cache_token_amd as pa
-from conftest import GOLDEN
+from conftest import GOLDEN, route_block_manager
+
+# under test_block_manager_sanitized.py: the pa_bm_* calls go to the
+# AddressSanitizer / UndefinedBehaviorSanitizer build of pa_blocks.cpp
+route_block_manager(pa)
 
 
 def test_allocate_slots_worked_example():

@@ -81,7 +81,8 @@ typedef enum pa_status {
   PA_ERR_WORKSPACE_TOO_SMALL = 4, /* workspace_bytes below the size query */
   PA_ERR_HIP = 5,                 /* the HIP runtime refused a launch */
   PA_ERR_NO_FREE_BLOCKS = 6,      /* block manager: the free queue is too short */
-  PA_ERR_HOST_MEMORY = 7          /* block manager: a host allocation failed */
+  PA_ERR_HOST_MEMORY = 7,         /* block manager: a host allocation failed */
+  PA_ERR_SCRATCH_TOO_SMALL = 8    /* pa_decode_noalloc: shapes beyond its fixed scratch */
 } pa_status;
 
 /* Library version as PA_VERSION. */
@@ -168,6 +169,37 @@ int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_c
                   int32_t block_size, int32_t max_blocks_per_seq, int32_t max_context_len,
                   int64_t num_blocks, float scale, int32_t dtype, void* workspace,
                   size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_noalloc -- pa_decode without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  It calls no allocator.
+ *
+ *   arguments        as pa_decode, minus workspace and workspace_bytes
+ *
+ * Same kernels, launch choice and result as pa_decode (bit-identical).  The
+ * split-K partials and work list live in a fixed device buffer of
+ * PA_NOALLOC_SCRATCH_BYTES (128 MiB) that the library holds on every GPU it
+ * runs on until the process ends; the first call on a device looks up that
+ * device's copy.  A call whose partials need more (num_seqs * num_q_heads *
+ * partitions * (head_dim + 2) * 4 bytes plus 8 bytes per work item, when some
+ * context spans several partitions; e.g. 128 sequences x 32 q heads with
+ * contexts up to 32768 tokens, 32 partitions of 1024, take 68 MB) returns
+ * PA_ERR_SCRATCH_TOO_SMALL and launches nothing.  Nothing in the buffer needs
+ * to start at zero: every value a call reads it has written earlier in the
+ * same call.  All calls on one GPU share the buffer, which keeps the last
+ * call's contents: calls that overlap in time on one GPU (several streams or
+ * threads) race and give wrong results, so serialise them.  Errors otherwise
+ * as pa_decode (PA_ERR_HIP also when the device's buffer cannot be found).
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (128u << 20)
+
+int32_t pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                          int32_t max_context_len, int64_t num_blocks, float scale, int32_t dtype,
+                          void* stream);
 
 /*
  * pa_decode_step -- one decode step in a single launch: store each sequence's

@@ -37,6 +37,8 @@ _SIGNATURES = {
     "pa_decode_workspace_size": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "pa_decode": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32,
                            _c_i32, _c_i32, _c_i32, _c_i64, _c_f32, _c_i32, _c_p, _c_sz, _c_p]),
+    "pa_decode_noalloc": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
+                                   _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_f32, _c_i32, _c_p]),
     "pa_decode_step": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32,
                                 _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_f32, _c_i32,
                                 _c_p, _c_sz, _c_p]),
@@ -250,6 +252,32 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         n, hq, hkv, d, bs, block_tables.shape[1], int(max_context_len), num_blocks, scale,
         _DTYPES[q.dtype], _ptr(workspace), ws_bytes, _stream(q)))
+    return out
+
+
+def decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                   scale: float | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """pa_decode with no workspace (pa_decode_noalloc): the library's fixed
+    per-GPU scratch holds the split-K partials.  Allocates nothing when
+    ``out`` is given; calls overlapping on one GPU race."""
+    for t, nm in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, nm)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    num_blocks, hkv, bs, d = _cache_dims(k_cache)
+    n, hq, dq = q.shape
+    if dq != d or q.dtype not in _DTYPES or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q / cache head_dim or dtype mismatch")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype)
+    _decode_shapes(q, out, k_cache, v_cache, block_tables, context_lens, None)
+    scale = float(d ** -0.5 if scale is None else scale)
+    _check("pa_decode_noalloc", lib.pa_decode_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        n, hq, hkv, d, bs, block_tables.shape[1], int(max_context_len), num_blocks, scale,
+        _DTYPES[q.dtype], _stream(q)))
     return out
 
 
@@ -506,6 +534,6 @@ class BlockManager:
 
 __all__ = ["BlockManager", "PAError", "swap_blocks", "PA_F32", "PA_BF16", "PA_ERR_NO_FREE_BLOCKS",
            "PA_ERR_HOST_MEMORY", "BLOCK_SIZE", "build_slot_mapping",
-           "cascade_decode", "cascade_workspace_size", "decode", "decode_step",
+           "cascade_decode", "cascade_workspace_size", "decode", "decode_noalloc", "decode_step",
            "decode_workspace_size", "header_functions", "lib", "status_string", "varlen_prefill",
            "varlen_workspace_size", "version", "write_kv"]

@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "../../include/pa.h"
 #include "pa_launch.h"
@@ -108,7 +109,7 @@ int cascade_max_parts(int32_t max_context_len, int32_t prefix_blocks, int part_t
 }
 
 
-// Host checks of a plain decode call (PA_OK: go on).
+// Host checks shared by pa_decode and pa_decode_noalloc (PA_OK: go on).
 int32_t decode_checks(void* out, const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_tables, const int32_t* context_lens,
                       int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -159,6 +160,58 @@ DecodeArgs decode_args(void* out, const void* q, const void* k_cache, const void
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Fixed device scratch of pa_decode_noalloc: the split-K partials and the work
+// list of a decode call, for callers that cannot allocate.  Every GPU the
+// library runs on holds one copy until the process ends.  In host code
+// `scratch` names a host-side stand-in, not device memory: the kernels get
+// the address hipGetSymbolAddress returns for the device, kept per device.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kScratchDevices = 64;  // device ordinals served by pa_decode_noalloc
+
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kScratchDevices];
+
+// The device `stream` runs on (the current device for the null stream).
+hipError_t stream_device(hipStream_t stream, int* dev) {
+  if (stream == nullptr) return hipGetDevice(dev);
+  hipDevice_t d = 0;
+  const hipError_t e = hipStreamGetDevice(stream, &d);
+  *dev = static_cast<int>(d);
+  return e;
+}
+
+// This device's copy of `scratch`, looked up once per device with that
+// device current (the current device is restored afterwards).
+hipError_t scratch_on(int dev, void** ptr) {
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  ScratchSlot& s = g_scratch[dev];
+  std::call_once(s.once, [&s, dev] {
+    int cur = -1;
+    s.err = hipGetDevice(&cur);
+    if (s.err == hipSuccess && cur != dev) s.err = hipSetDevice(dev);
+    if (s.err == hipSuccess) s.err = hipGetSymbolAddress(&s.ptr, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != dev) {
+      const hipError_t r = hipSetDevice(cur);
+      if (s.err == hipSuccess) s.err = r;
+    }
+    if (s.err == hipSuccess && s.ptr == nullptr) s.err = hipErrorInvalidSymbol;
+    if (s.err != hipSuccess) (void)hipGetLastError();
+  });
+  *ptr = s.ptr;
+  return s.err;
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t pa_version(void) { return PA_VERSION; }
@@ -175,6 +228,8 @@ const char* pa_status_string(int32_t status) {
     case PA_ERR_HIP: return "the HIP runtime rejected a kernel launch";
     case PA_ERR_NO_FREE_BLOCKS: return "not enough free blocks in the pool";
     case PA_ERR_HOST_MEMORY: return "a host memory allocation failed";
+    case PA_ERR_SCRATCH_TOO_SMALL:
+      return "the call needs more than the fixed device scratch of pa_decode_noalloc";
     default: return "unknown status";
   }
 }
@@ -270,6 +325,37 @@ int32_t pa_decode(void* out, const void* q, const void* k_cache, const void* v_c
                              max_context_len, num_blocks, scale, dtype);
   if (a.max_parts > 1)
     a.ws = decode_ws_layout(workspace, num_seqs, num_q_heads, head_dim, a.max_parts);
+  return from_hip(launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+int32_t pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                          int32_t max_context_len, int64_t num_blocks, float scale, int32_t dtype,
+                          void* stream) {
+  const int32_t st = decode_checks(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                                   num_q_heads, num_kv_heads, head_dim, block_size,
+                                   max_blocks_per_seq, max_context_len, num_blocks, scale, dtype);
+  if (st != PA_OK || num_seqs == 0) return st;
+  DecodeArgs a = decode_args(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                             num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                             max_context_len, num_blocks, scale, dtype);
+  if (a.max_parts > 1) {
+    // what this launch uses (its own partition length, not the size query's
+    // shortest one), refused before anything is enqueued when it exceeds the
+    // fixed buffer
+    const size_t need = decode_ws_bytes(num_seqs, num_q_heads, head_dim, a.max_parts);
+    if (need > (size_t)PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_SCRATCH_TOO_SMALL;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    int dev = -1;
+    void* base = nullptr;
+    if (stream_device(hs, &dev) != hipSuccess || scratch_on(dev, &base) != hipSuccess) {
+      (void)hipGetLastError();
+      return PA_ERR_HIP;
+    }
+    a.ws = decode_ws_layout(base, num_seqs, num_q_heads, head_dim, a.max_parts);
+  }
   return from_hip(launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -19,7 +19,12 @@ step reads K/V that the previous one left in the 256 MB Infinity Cache.
 Prints one JSON line.  `value` is the step's algorithmic HBM bytes over its
 time (GB/s); `roofline` covers the attention kernel, timed with HIP events on
 the stream it is launched on; `cpu_baseline` is the float64 CPU oracle timed on
-a bounded sample of the same workload on this host.
+a bounded sample of the same workload on this host, over a pool of worker
+processes.  The default run adds `configs`: one sub-record (value, unit,
+roofline, cpu_baseline, step time, graph replay) for each other configuration
+-- the tiny fp32 decode, GQA decode, the mixed step (whole call) and its
+prefill chunks alone (TFLOP/s against the matrix-core peak), and the
+shared-prefix decode through pa_decode_step and through pa_cascade_decode.
 """
 from __future__ import annotations
 
@@ -38,7 +43,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode KV-read GB/s (% of HBM peak); prefill TFLOP/s; seq-steps/s"
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
-MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak
+MFMA_BF16_PEAK_TFS = 2516.6  # MI355X dense bf16 matrix peak
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "decode": ["paged_kv_cache_token_amd/csrc/pa_decode.hip",
@@ -123,46 +128,103 @@ def prefill_flops(b) -> int:
 
 
 # --------------------------------------------------------------------------
-# CPU baseline: the float64 oracle on a bounded sample
+# CPU baseline: the float64 oracle on a bounded sample, over all host cores
 # --------------------------------------------------------------------------
 
-def cpu_baseline(b, budget_s: float = 10.0) -> dict:
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    import oracle
-    from oracle_side import expected, host_state
+_CPU = {}  # the batch and host state the forked workers read (copy-on-write)
 
+
+def _cpu_init():
+    # one BLAS thread per worker: the pool supplies the parallelism
+    try:
+        import threadpoolctl
+        threadpoolctl.threadpool_limits(1)
+    except Exception:
+        pass
+
+
+def _cpu_seq(i):
+    from oracle_side import expected
+    expected(_CPU["b"], _CPU["hs"], seqs=[i])
+    return i
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_workers() -> int:
+    """Worker processes: the host cores this process may run on, at most 16
+    (the CPU share of one GPU on a shared host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_baseline(b, budget_s: float = 10.0, unit: str = "GB/s") -> dict:
+    """The float64 oracle (tests/oracle_side.py) on host copies of the same
+    inputs, one sequence per task over a process pool (one BLAS thread per
+    worker), for about budget_s seconds of wall time; `unit` GB/s (the same
+    algorithmic bytes as the GPU figure) or TFLOP/s (causal prefill pairs)."""
+    import multiprocessing as mp
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from oracle_side import host_state
+
+    t_setup = time.perf_counter()
     hs = host_state(b, device="cuda")
+    setup_s = time.perf_counter() - t_setup
+    _CPU["b"], _CPU["hs"] = b, hs
     n = b.num_seqs
-    order = list(range(n))
-    done_seqs = 0
-    done_bytes = 0
-    per_seq_bytes = _per_seq_attention_bytes(b)
-    t0, c0 = time.perf_counter(), time.process_time()
-    passes = 0
-    while True:
-        for i in order:
-            expected(b, hs, seqs=[i])
-            done_seqs += 1
-            done_bytes += per_seq_bytes[i]
-            if time.perf_counter() - t0 >= budget_s and done_seqs >= min(n, 8):
+    work_bytes = _per_seq_attention_bytes(b)
+    work_flops = _per_seq_prefill_flops(b)
+    workers = cpu_workers()
+    # sequences in a fixed shuffled order (long and short mixed), repeated
+    order = list(np.random.default_rng(0).permutation(n))
+    done, done_bytes, done_flops, passes = 0, 0, 0, 0
+    ctx = mp.get_context("fork")  # workers only run numpy on inherited host arrays
+    with ctx.Pool(workers, initializer=_cpu_init) as pool:
+        t0 = time.perf_counter()
+        # tasks taken as workers free up; counted as they finish, up to the
+        # budget (the pool is terminated with the tasks still in flight)
+        tasks = (order[k % n] for k in range(n * 1000))
+        for i in pool.imap_unordered(_cpu_seq, tasks, chunksize=1):
+            done += 1
+            done_bytes += work_bytes[i]
+            done_flops += work_flops[i]
+            if time.perf_counter() - t0 >= budget_s and done >= min(n, 8):
                 break
-        else:
-            passes += 1
-            continue
-        break
-    wall = time.perf_counter() - t0
-    cpu = time.process_time() - c0
-    del oracle
+        wall = time.perf_counter() - t0
+        passes = done // n
+    _CPU.clear()
+    del hs
+    value = done_bytes / wall / 1e9 if unit == "GB/s" else done_flops / wall / 1e12
     return {
-        "value": round(done_bytes / wall / 1e9, 4),
-        "unit": "GB/s",
-        "cores": max(1, int(round(cpu / wall))),
+        "value": round(value, 4 if unit == "GB/s" else 6),
+        "unit": unit,
+        "cores": workers,
         "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": (f"float64 numpy oracle ({'decode' if b.kind == 'decode' else 'varlen_prefill'})"
-                   f" over {done_seqs} sequences of the workload ({passes} full passes), "
-                   f"{wall:.1f} s wall, {cpu:.1f} s CPU"),
-        "seq_steps_per_s": round(done_seqs / wall, 3),
+                   f" over {done} sequences of the workload ({passes} full passes), "
+                   f"{workers} worker processes x 1 BLAS thread, {wall:.1f} s wall "
+                   f"(+{setup_s:.1f} s building the host copy of the inputs)"),
+        "seq_steps_per_s": round(done / wall, 3),
     }
+
+
+def _per_seq_prefill_flops(b) -> list[int]:
+    out = []
+    for c, l in zip(b.context_offsets.astype(np.int64), b.q_lens.astype(np.int64)):
+        out.append(int(4 * b.num_q_heads * b.head_dim * (l * c + l * (l + 1) // 2)) if l > 1 else 0)
+    return out
 
 
 def _per_seq_attention_bytes(b) -> list[int]:
@@ -195,10 +257,7 @@ def traffic_from_profiles(workload: str, kind: str):
 def context_figures(dbs, run_step, stream, steps, dev) -> dict:
     """Figures reported beside the measurement, none of them `value`: the
     warm median (every step on the same layer's caches, so K/V may sit in
-    the 256 MB MALL), a plain device copy's bandwidth, and the step replayed
-    from HIP graphs (one captured step per layer cache; the library makes no
-    allocation, synchronisation or memset, so a captured call is the same
-    launches)."""
+    the 256 MB MALL) and a plain device copy's and read's bandwidth."""
     import torch
     out = {}
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -233,7 +292,17 @@ def context_figures(dbs, run_step, stream, steps, dev) -> dict:
     torch.cuda.synchronize()
     out["read_gbs_sum_1gib"] = round(n * reps / (a.elapsed_time(z) * 1e-3) / 1e9, 1)
     del src, dst, x
+    return out
 
+
+def graph_figures(dbs, run_step, stream, steps) -> dict:
+    """The step replayed from HIP graphs (the library makes no allocation,
+    synchronisation or memset, so a captured call is the same launches):
+    every layer's step captured into one graph, as a model's forward pass
+    would be, and, for comparison, one graph per layer's step."""
+    import torch
+    out = {}
+    a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     try:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -242,22 +311,35 @@ def context_figures(dbs, run_step, stream, steps, dev) -> dict:
                 run_step(d)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        graphs = []
+        whole = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(whole):
+            for d in dbs:
+                run_step(d)
+        per_layer = []
         for d in dbs:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 run_step(d)
-            graphs.append(g)
-        for g in graphs:
+            per_layer.append(g)
+        whole.replay()
+        for g in per_layer:
             g.replay()
         torch.cuda.synchronize()
+        reps = max(1, -(-steps // len(dbs)))
         a.record(stream)
-        for s in range(steps):
-            graphs[s % len(graphs)].replay()
+        for _ in range(reps):
+            whole.replay()
         z.record(stream)
         torch.cuda.synchronize()
-        out["graph_ms_per_step"] = round(a.elapsed_time(z) / steps, 5)
-        del graphs
+        out["graph_ms_per_step"] = round(a.elapsed_time(z) / (reps * len(dbs)), 5)
+        a.record(stream)
+        for s in range(steps):
+            per_layer[s % len(per_layer)].replay()
+        z.record(stream)
+        torch.cuda.synchronize()
+        out["graph_ms_per_step_one_graph_per_step"] = round(a.elapsed_time(z) / steps, 5)
+        out["graph_layers_per_replay"] = len(dbs)
+        del whole, per_layer
     except Exception as e:  # reported, never fatal: the eager figures stand alone
         out["graph_ms_per_step"] = None
         out["graph_error"] = str(e)[:200]
@@ -412,52 +494,23 @@ def bench_block_manager(args) -> int:
     return 0
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="llama2_decode",
-                    choices=["llama2_decode", "gqa_decode", "shared_prefix_decode",
-                             "shared_prefix_cascade", "long_prefix_decode",
-                             "long_prefix_cascade", "mixed_step", "prefill_chunks", "prefill_long",
-                             "tiny_decode", "block_swap", "block_manager"])
-    ap.add_argument("--layers", type=int, default=0,
-                    help="layer caches to rotate through (0: enough for >= 1 GiB)")
-    ap.add_argument("--cpu-budget", type=float, default=10.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--unfused", action="store_true",
-                    help="decode: three calls (slot mapping, write, decode) instead of one")
-    ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="also run one plain device copy of this size (counter calibration)")
-    ap.add_argument("--no-extras", action="store_true",
-                    help="skip the context figures (warm median, copy bandwidth, graph replay)")
-    args = ap.parse_args()
+# configurations carried as sub-records of the default run's line: every
+# configuration the metric is quoted on, beside the LLaMA-2 decode headline
+SUB_WORKLOADS = ["tiny_decode", "gqa_decode", "mixed_step", "prefill_chunks",
+                 "shared_prefix_decode", "shared_prefix_cascade"]
 
-    if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
-                          "n_gpus": args.gpus}))
-        return 2
 
+def measure(name: str, args, dev, headline: bool) -> dict:
+    """Time `args.steps` steps of one workload; the record of its line (the
+    headline) or of its sub-record."""
     import torch
 
-    import paged_kv_cache_token_amd as pa  # fails loudly if libpa.so is missing
     from device_batch import DeviceBatch
 
-    if args.workload == "block_manager":
-        return bench_block_manager(args)  # host code only
-    if not torch.cuda.is_available():
-        print(json.dumps({"error": "no GPU visible"}))
-        return 2
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
-    if args.workload == "block_swap":
-        return bench_block_swap(args, dev)
-    b = make_batch(args.workload)
+    b = make_batch(name)
     kind = "decode" if b.kind == "decode" else "prefill"
     # the shared-prefix batch through pa_cascade_decode (new tokens stored first)
-    cascade = args.workload.endswith("_cascade")
+    cascade = name.endswith("_cascade")
     fused = kind == "decode" and not args.unfused and not cascade
     att_bytes = attention_bytes(b)
     # the fused step reads the new K/V rows and stores them: no slot array traffic
@@ -467,7 +520,7 @@ def main() -> int:
     dbs = [DeviceBatch(b.with_layer(l), device=dev) for l in range(layers)]
     torch.cuda.synchronize()
 
-    if args.calib_copy_mib:
+    if args.calib_copy_mib and headline:
         src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
@@ -526,46 +579,50 @@ def main() -> int:
 
     extras = {}
     if not args.no_extras:
-        extras = context_figures(dbs, run_step, stream, args.steps, dev)
+        if headline:
+            extras.update(context_figures(dbs, run_step, stream, args.steps, dev))
+        extras.update(graph_figures(dbs, run_step, stream, args.steps))
 
     step_bytes = att_bytes + wr_bytes
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    fl = prefill_flops(b)
+    prefill_only = kind == "prefill" and int((b.q_lens == 1).sum()) == 0
+    if prefill_only:
+        unit = "TFLOP/s"
+        value = fl / (ms_per_step * 1e-3) / 1e12
+    else:
+        unit = "GB/s"
+        value = step_bytes / (ms_per_step * 1e-3) / 1e9
     # the dominant kernel's average duration: with the fused decode step a step
-    # is exactly one launch of it, so timed region 1 gives it without the
-    # per-launch event overhead; otherwise the event pairs of region 2
+    # is exactly one launch of it (single-partition contexts), so timed region 1
+    # gives it without the per-launch event overhead; otherwise the event pairs
+    # of region 2 (the whole attention call)
     kern_ms = ms_per_step if fused else att_avg_ms
-    if kind == "decode" or args.workload == "mixed_step":
+    if not prefill_only:
         kern_bytes = att_bytes + (wr_bytes if fused else 0)
         achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
-        traffic = traffic_from_profiles(args.workload, "decode")
+        traffic = traffic_from_profiles(name, "cascade" if cascade else "decode")
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": traffic}
     else:
-        fl = prefill_flops(b)
         achieved = fl / (att_avg_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFS,
                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4),
-                    "traffic": traffic_from_profiles(args.workload, "prefill")}
+                    "traffic": traffic_from_profiles(name, "prefill")}
 
+    del dbs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(b, args.cpu_budget)
+        cpu = cpu_baseline(b, args.cpu_budget if headline else args.sub_cpu_budget, unit)
 
     ctx = b.context_lens
     rec = {
-        "metric": METRIC,
-        "value": round(value, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "value": round(value, 1 if unit == "GB/s" else 2),
+        "unit": unit,
         "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
         "dtype": "bf16" if b.dtype == "bf16" else "f32",
-        "data": "synthetic",
         "config": {
             "workload": b.name,
             "num_seqs": b.num_seqs,
@@ -587,19 +644,94 @@ def main() -> int:
         "step_calls": "pa_decode_step (fused)" if fused else (
             "pa_build_slot_mapping + pa_write_kv + " +
             ("pa_cascade_decode" if cascade else
-             "pa_decode" if kind == "decode" else "pa_varlen_prefill")),
+             "pa_decode" if kind == "decode" else "pa_varlen_prefill_ex")),
         "attention_bytes": att_bytes,
         "write_bytes": wr_bytes,
         "step_bytes": step_bytes,
         "wall_s_timed": round(wall, 4),
         "kernel_source_hash": kernel_hash("cascade" if cascade else kind),
-        "call_us_p10_p50_p90": [round(float(np.percentile(att_ms, q)) * 1e3, 2) for q in (10, 50, 90)],
+        "call_us_p10_p50_p90": [round(float(np.percentile(att_ms, q)) * 1e3, 2)
+                                for q in (10, 50, 90)],
     }
-    rec.update(extras)
-    if kind == "prefill" or args.workload == "mixed_step":
-        fl = prefill_flops(b)
+    if b.notes.get("prefix_tokens") and not b.notes.get("unshared"):
+        rec["logical_kv_bytes"] = 2 * int(ctx.astype(np.int64).sum()) * b.num_kv_heads * \
+            b.head_dim * b.elem_bytes
+    if kind == "prefill":
         rec["prefill_flops"] = fl
         rec["prefill_tflops_whole_call"] = round(fl / (att_avg_ms * 1e-3) / 1e12, 2)
+    rec.update(extras)
+    return rec
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama2_decode",
+                    choices=["llama2_decode", "gqa_decode", "shared_prefix_decode",
+                             "shared_prefix_cascade", "long_prefix_decode",
+                             "long_prefix_cascade", "mixed_step", "prefill_chunks", "prefill_long",
+                             "tiny_decode", "block_swap", "block_manager"])
+    ap.add_argument("--layers", type=int, default=0,
+                    help="layer caches to rotate through (0: enough for >= 1 GiB)")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle time for the headline's CPU baseline")
+    ap.add_argument("--sub-cpu-budget", type=float, default=6.0,
+                    help="seconds of oracle time for each sub-record's CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="the default workload alone, without the other configurations")
+    ap.add_argument("--unfused", action="store_true",
+                    help="decode: three calls (slot mapping, write, decode) instead of one")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (counter calibration)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the context figures (warm median, copy bandwidth, graph replay)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        return 2
+
+    import torch
+
+    import paged_kv_cache_token_amd as pa  # fails loudly if libpa.so is missing
+    del pa
+
+    if args.workload == "block_manager":
+        return bench_block_manager(args)  # host code only
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.workload == "block_swap":
+        return bench_block_swap(args, dev)
+    head = measure(args.workload, args, dev, headline=True)
+    rec = {
+        "metric": METRIC,
+        "value": head.pop("value"),
+        "unit": head.pop("unit"),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head.pop("ms_per_step"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head.pop("dtype"),
+        "data": "synthetic",
+    }
+    rec.update(head)
+    if args.workload == "llama2_decode" and not args.headline_only:
+        subs = {}
+        for w in SUB_WORKLOADS:
+            print(f"[bench] {w}", file=sys.stderr, flush=True)
+            subs[w] = measure(w, args, dev, headline=False)
+        rec["configs"] = subs
     print(json.dumps(rec), flush=True)
     return 0
 

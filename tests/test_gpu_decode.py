@@ -151,29 +151,28 @@ def test_llama2_decode_full(gpu):
     _check_decode(W.llama2_decode())
 
 
-def test_gqa_decode_full_sampled(gpu):
-    batch = W.gqa_decode()
-    order = np.argsort(batch.context_lens)
-    seqs = sorted(set(order[:4].tolist() + order[-6:].tolist() + list(range(0, 256, 23))))
-    _check_decode(batch, seqs=seqs, check_pools=False)
+def test_gqa_decode_full(gpu):
+    """GQA decode (256 sequences, Pareto lengths up to 4096): every row
+    against the oracle, pools bit-exact."""
+    _check_decode(W.gqa_decode())
 
 
-def test_many_pairs_single_partition_sampled(gpu):
+def test_many_pairs_single_partition(gpu):
     """>= 4096 (sequence, kv head) pairs with contexts past one 512-token
-    partition: the launch keeps each context in one partition."""
+    partition: the launch keeps each context in one partition.  Every row
+    against the oracle."""
     rng = np.random.default_rng(28)
     lens = rng.integers(16, 1500, size=520)
     batch = W.decode_batch("many_pairs", 28, lens, 32, 8, 128, "bf16")
-    order = np.argsort(batch.context_lens)
-    seqs = sorted(set(order[:3].tolist() + order[-5:].tolist() + list(range(0, 520, 37))))
-    _check_decode(batch, seqs=seqs, check_pools=False)
+    _check_decode(batch, check_pools=False)
 
 
-def test_shared_prefix_full_sampled_and_unshared(gpu):
+def test_shared_prefix_full_and_unshared(gpu):
+    """Shared-prefix decode (128 sequences whose tables share 64 blocks,
+    contexts up to 32768): every row against the oracle, and bit-identical
+    to the same tokens laid out with a private copy of the prefix each."""
     shared = W.shared_prefix_decode()
-    order = np.argsort(shared.context_lens)
-    seqs = sorted(set([0, 1, 64, 127] + order[:2].tolist() + order[-2:].tolist()))
-    _, out_s = _check_decode(shared, seqs=seqs, check_pools=False)
+    _, out_s = _check_decode(shared, check_pools=False)
     out_s = out_s.clone()
     torch.cuda.empty_cache()
     out_u = _device_batch(W.shared_prefix_decode(unshared=True)).step()
@@ -334,13 +333,12 @@ def test_decode_launch_variants(gpu, monkeypatch, env):
 @pytest.mark.parametrize("n,max_len", [(1100, 256), (600, 500)])
 def test_decode_many_short_contexts(gpu, n, max_len):
     """Batches of many short contexts run one or two waves per item (no
-    cross-wave merge for one): sampled rows against the oracle."""
+    cross-wave merge for one): every row against the oracle."""
     rng = np.random.default_rng(37 + n)
     lens = rng.integers(1, max_len + 1, size=n)
     lens[0] = max_len
     batch = W.decode_batch(f"short_{n}", 37, lens, 32, 8, 128, "bf16", pool_factor=1.2)
-    seqs = sorted(set([0, 1, n - 1] + rng.choice(n, size=40, replace=False).tolist()))
-    _check_decode(batch, seqs=seqs, check_pools=False)
+    _check_decode(batch, check_pools=False)
 
 
 @pytest.mark.parametrize("dtype,d,hq,hkv,n", [("bf16", 128, 32, 8, 160), ("f32", 64, 8, 8, 130)])
@@ -372,5 +370,4 @@ def test_decode_list_beyond_inline_plan(gpu):
     lens = rng.integers(1, 65, size=2100)
     lens[7] = 5000
     batch = W.decode_batch("list_2100", 38, lens, 32, 8, 128, "bf16", pool_factor=1.2)
-    seqs = sorted(set([0, 7, 2099] + rng.choice(2100, size=30, replace=False).tolist()))
-    _check_decode(batch, seqs=seqs, check_pools=False)
+    _check_decode(batch, check_pools=False)

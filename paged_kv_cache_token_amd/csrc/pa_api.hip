@@ -61,9 +61,7 @@ size_t varlen_rows_bytes(int32_t total_q) {
   return align_up((size_t)total_q * sizeof(int32_t));
 }
 size_t varlen_work_bytes(int32_t num_seqs, int32_t total_q, int32_t hkv, int32_t group) {
-  // count and pad, then two ints per item
-  return align_up((size_t)(2 + 2 * (size_t)prefill_work_capacity(num_seqs, total_q, hkv, group)) *
-                  sizeof(int32_t));
+  return align_up(prefill_work_bytes(num_seqs, total_q, hkv, group));
 }
 
 // The common-prefix pass runs on the matrix-core kernel: bf16 at head_dim 128.

@@ -36,6 +36,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // rows per prefill work item and bound on the number of items
 int prefill_tile_tokens(int group);
 int prefill_work_capacity(int num_seqs, int total_q_tokens, int num_kv_heads, int group);
+// bytes of the work list (header and one record per item) in the workspace
+size_t prefill_work_bytes(int num_seqs, int total_q_tokens, int num_kv_heads, int group);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 // the common-prefix pass: `splits` items per (row tile, kv head)
 hipError_t launch_cascade_prefix(const PrefillArgs& a, int splits, hipStream_t stream);

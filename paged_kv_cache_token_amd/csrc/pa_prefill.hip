@@ -20,7 +20,11 @@
 //     [block][16-byte chunk][key], keys swizzled by chunk; V is read back with
 //     the transposing LDS read).  One barrier per tile: tile t is computed
 //     while tile t+1 waits in LDS and the loads of tile t+2 are in flight;
-//   * the work list is ordered longest first (key tiles per item);
+//   * the work list is ordered longest first (key tiles per item); one
+//     workgroup per CU walks its share in snake order, and while an item runs
+//     its last steps the next item's record, first two key tiles and query
+//     rows are already being loaded, so items follow each other without a
+//     cold start;
 //   * scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = the wave's 32 query rows
 //     held in registers), so a lane holds 16 scores of one query row and the
@@ -63,10 +67,24 @@ int prefill_work_capacity(int num_seqs, int total_q_tokens, int num_kv_heads, in
   return (total_q_tokens / t + num_seqs + 1) * num_kv_heads;
 }
 
-// Work list in the workspace: int32 count, int32 pad, then int2
-// (seq, tile * num_kv_heads + kv head).
-__device__ __forceinline__ int2* prefill_items(int32_t* work) {
-  return reinterpret_cast<int2*>(work + 2);
+// Work list in the workspace: a 64-byte header (int32 item count), then one
+// 128-byte record per item, int32 words:
+//   [0] sequence  [1] query tile * num_kv_heads + kv head  [2] first packed row
+//   [3] query rows of the sequence  [4] its cached tokens  [5..7] unused
+//   [8 + 4j + b]  table entry of block b of key tile j, j < 3 (clamped into
+//                 the table row), so a workgroup can start the item's first
+//                 tile loads without reading the table itself
+constexpr int kRecWords = 32;
+constexpr int kWorkHeaderWords = 16;
+
+__device__ __forceinline__ int32_t* prefill_rec(int32_t* work, int idx) {
+  return work + kWorkHeaderWords + (int64_t)idx * kRecWords;
+}
+
+size_t prefill_work_bytes(int num_seqs, int total_q_tokens, int num_kv_heads, int group) {
+  return (kWorkHeaderWords +
+          (size_t)kRecWords * prefill_work_capacity(num_seqs, total_q_tokens, num_kv_heads, group)) *
+         sizeof(int32_t);
 }
 
 // One workgroup lists the (sequence, query tile, kv head) items of every
@@ -178,11 +196,22 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillArgs 
   count[kSortBuckets - 1 - t] = off;
   if (t == 0) a.work[0] = min(total, a.work_cap);
   __syncthreads();
-  int2* items = prefill_items(a.work);
   auto place = [&](int sq, int q, int len, int c) {
     const int pos = atomicAdd(&count[bucket(len, c, q)], a.num_kv_heads);
-    for (int h = 0; h < a.num_kv_heads; ++h)
-      if (pos + h < a.work_cap) items[pos + h] = make_int2(sq, q * a.num_kv_heads + h);
+    const int32_t* table = a.block_tables + (int64_t)sq * a.max_blocks_per_seq;
+    int e[12];
+#pragma unroll
+    for (int i = 0; i < 12; ++i) e[i] = table[min(i, a.max_blocks_per_seq - 1)];
+    const int lo = a.cu_seqlens[sq];
+    for (int h = 0; h < a.num_kv_heads; ++h) {
+      if (pos + h >= a.work_cap) break;
+      int4* r = reinterpret_cast<int4*>(prefill_rec(a.work, pos + h));
+      r[0] = make_int4(sq, q * a.num_kv_heads + h, lo, len);
+      r[1] = make_int4(c, 0, 0, 0);
+      r[2] = make_int4(e[0], e[1], e[2], e[3]);
+      r[3] = make_int4(e[4], e[5], e[6], e[7]);
+      r[4] = make_int4(e[8], e[9], e[10], e[11]);
+    }
   };
   if (fits) {
     for (int p = t; p < npairs; p += kPlanThreads) {
@@ -238,12 +267,105 @@ __device__ __forceinline__ uint2 lds_read_tr(const uint16_t* p) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(PA_LDS(i16x4_t, p)));
 }
 
-// A prefill work item's metadata, and the table entries of its first two key
-// tiles (one per lane, lane i: block i & 3 of the tile).
+// A prefill work item's metadata, and the table entries of its first three
+// key tiles (one per lane, lane i: block i & 3 of the tile).
 struct ItemMeta {
   int seq, qtile, kvh;  // cascade: key split, row tile, kv head
   int lo_row, len, c;   // first packed row, query rows, cached tokens
-  int e0, e1;
+  int e0, e1, e2;
+};
+
+// An item's record as loaded (vector registers), turned into ItemMeta only
+// where it is used, so the load is waited for there and not at issue.
+struct RecRaw {
+  int4 m;  // seq, tile * num_kv_heads + kv head, first row, query rows
+  int c, e0, e1, e2;
+};
+
+__device__ __forceinline__ RecRaw load_rec(const PrefillArgs& a, int idx) {
+  const int32_t* r = prefill_rec(a.work, idx);
+  const int lane = threadIdx.x & 63;
+  RecRaw x;
+  x.m = *reinterpret_cast<const int4*>(r);
+  x.c = r[4];
+  x.e0 = r[8 + (lane & 3)];
+  x.e1 = r[12 + (lane & 3)];
+  x.e2 = r[16 + (lane & 3)];
+  return x;
+}
+
+__device__ __forceinline__ ItemMeta meta_of(const PrefillArgs& a, const RecRaw& x) {
+  ItemMeta im;
+  im.seq = __builtin_amdgcn_readfirstlane(x.m.x);
+  const int y = __builtin_amdgcn_readfirstlane(x.m.y);
+  im.qtile = y / a.num_kv_heads;
+  im.kvh = y - im.qtile * a.num_kv_heads;
+  im.lo_row = __builtin_amdgcn_readfirstlane(x.m.z);
+  im.len = __builtin_amdgcn_readfirstlane(x.m.w);
+  im.c = __builtin_amdgcn_readfirstlane(x.c);
+  im.e0 = x.e0;
+  im.e1 = x.e1;
+  im.e2 = x.e2;
+  return im;
+}
+
+// Keys [0, kend) that any row of a (non-cascade) item sees, clamped to the
+// declared maxima.
+template <int G>
+__device__ __forceinline__ int item_kend(const PrefillArgs& a, const ItemMeta& x) {
+  constexpr int BMT = kPrefillRows / G;
+  const int q0 = x.qtile * BMT;
+  const int qn = min(BMT, x.len - q0);
+  const int kmax = min(a.max_context_len, a.max_blocks_per_seq * kBlockSize);
+  return max(0, min(x.c + q0 + qn, kmax));
+}
+
+// The query fragments of item x (B operand of S^T = K Q^T): lane n = lane & 31
+// of wave w holds row rho = 32w + n (head kvh*G + rho / (256/G), token
+// q0 + rho % (256/G)), dims ks*16 + hi*8 .. +8 in qf[ks].  Rows past the tile
+// or outside the packed arrays read as zeros.  A call with scale < 0 runs on
+// -q and |scale| (negating a bf16 flips its sign bit: exact), one with scale 0
+// on q = 0 (all scores 0: uniform weights).
+template <int G, bool CASCADE>
+__device__ __forceinline__ void load_query(const PrefillArgs& a, const ItemMeta& x,
+                                           bf16x8_t (&qf)[8]) {
+  constexpr int D = kPrefillD;
+  constexpr int BMT = kPrefillRows / G;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31, hi = lane >> 5;
+  const int lo_row = CASCADE ? 0 : x.lo_row;
+  const int len = CASCADE ? a.num_seqs : x.len;
+  const int q0 = x.qtile * BMT;
+  const int qn = min(BMT, len - q0);
+  const int rho = wave * 32 + n;
+  const int head = x.kvh * G + rho / BMT;
+  const int tok = rho % BMT;
+  const bool valid =
+      tok < qn && lo_row >= 0 && (int64_t)lo_row + q0 + tok < (int64_t)a.total_q_tokens;
+  const uint4* qrow = static_cast<const uint4*>(a.q) +
+                      ((int64_t)(valid ? lo_row + q0 + tok : 0) * a.num_q_heads + head) * (D / 8);
+  const uint32_t flip = a.q_sign < 0 ? 0x80008000u : 0u;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    uint4 v = qrow[ks * 2 + hi];
+    v.x ^= flip;
+    v.y ^= flip;
+    v.z ^= flip;
+    v.w ^= flip;
+    if (!valid || a.q_sign == 0) v = make_uint4(0u, 0u, 0u, 0u);
+    qf[ks] = __builtin_bit_cast(bf16x8_t, v);
+  }
+}
+
+// What a workgroup carries from one item to the next.
+struct PipeState {
+  bf16x8_t qf[8];  // the query fragments of the item about to run, when q_ready
+  int tb;          // key tiles this workgroup has streamed: tile t of the
+                   // running item sits in LDS buffer (tb + t) & 3
+  int pre;         // leading key tiles (0..2) of the item about to run whose
+                   // loads the previous item already issued
+  bool q_ready;
 };
 
 // One work item.  Prefill (CASCADE = false): sequence `seq`, query tile
@@ -252,9 +374,18 @@ struct ItemMeta {
 // the rows are (q head, sequence) for sequences qtile*256/G ..; every row
 // sees the prefix keys below its own context length, and the item writes
 // unnormalised partials instead of the output.
+//
+// Items run back to back in a workgroup overlap their start-up with the end
+// of the previous item: given the next item's index, the running one loads
+// its record with its own first key tile, starts the next item's first two
+// key tiles into the LDS buffers its own last two steps leave free, and loads
+// the next item's queries during its own last step (which skips the discarded
+// score products that would read them).  On return `next` holds the next
+// item and `pipe` what was started for it.
 template <int G, bool CASCADE>
 __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const ItemMeta& im,
-                                             PrefillShared& sm) {
+                                             PrefillShared& sm, PipeState& pipe, int next_idx,
+                                             ItemMeta& next) {
   const int seq = im.seq, qtile = im.qtile, kvh = im.kvh;
   constexpr int D = kPrefillD;
   constexpr int BMT = kPrefillRows / G;  // query tokens per item
@@ -309,25 +440,15 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const ItemMet
   const int hq = a.num_q_heads;
   const int32_t* table = a.block_tables + (CASCADE ? 0 : (int64_t)seq * a.max_blocks_per_seq);
 
-  // B operand of S^T = K Q^T: this lane's query row, dims ks*16 + hi*8 .. +8
-  bf16x8_t qf[8];
-  {
-    const uint4* qrow = static_cast<const uint4*>(a.q) +
-                        ((int64_t)(valid_q ? lo_row + q0 + tok : 0) * hq + head) * (D / 8);
-    // a call with scale < 0 runs on -q and |scale| (negating a bf16 flips its
-    // sign bit: exact), one with scale 0 on q = 0 (all scores 0: uniform weights)
-    const uint32_t flip = a.q_sign < 0 ? 0x80008000u : 0u;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      uint4 v = qrow[ks * 2 + hi];
-      v.x ^= flip;
-      v.y ^= flip;
-      v.z ^= flip;
-      v.w ^= flip;
-      if (!valid_q || a.q_sign == 0) v = make_uint4(0u, 0u, 0u, 0u);
-      qf[ks] = __builtin_bit_cast(bf16x8_t, v);
-    }
-  }
+  // B operand of S^T = K Q^T: this item's query rows (already loaded when the
+  // previous item prefetched them)
+  bf16x8_t (&qf)[8] = pipe.qf;
+  if (!pipe.q_ready) load_query<G, CASCADE>(a, im, qf);
+  const int tb = pipe.tb;
+  const bool has_next = !CASCADE && next_idx >= 0;
+  RecRaw nraw{};
+  int next_pre = 0;       // leading tiles of the next item started here
+  bool next_q = false;    // the next item's queries loaded here
 
   // Table entries of a tile, one per lane (lane i & 3: block i & 3 of the
   // tile), loaded one step ahead with vector loads that land with that step's
@@ -363,7 +484,9 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const ItemMet
     const int ch = 4 * ((2 * wave + r) & 3) + (lane >> 4);
     dma_off[r] = ((lane & 15) ^ (4 * (ch & 3))) * kRowBytes + ch * 16;
   }
-  auto issue = [&](int t, int b, int e) {
+  // key tile `tile` (absolute) of an item with keys [0, kend_x) of kv head
+  // kvh_x, into LDS buffer b
+  auto issue_for = [&](int kend_x, int kvh_x, int tile, int b, int e) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int j = 2 * wave + r;
@@ -371,12 +494,13 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const ItemMet
       const int phys = phys_of(e, blk);              // wave-uniform
       // (readfirstlane: a buffer descriptor must be scalar)
       const int nvalid = __builtin_amdgcn_readfirstlane(
-          phys < 0 ? 0 : min(max(kend - ((tile0 + t) * kKeyTile + blk * kBlockSize), 0), kBlockSize));
-      const int64_t off = ((int64_t)max(phys, 0) * hkv + kvh) * (kBlockSize * kRowBytes);
+          phys < 0 ? 0 : min(max(kend_x - (tile * kKeyTile + blk * kBlockSize), 0), kBlockSize));
+      const int64_t off = ((int64_t)max(phys, 0) * hkv + kvh_x) * (kBlockSize * kRowBytes);
       dma16(kc + off, nvalid * kRowBytes, dma_off[r], &sm.k[b][blk][c0][0]);
       dma16(vc + off, nvalid * kRowBytes, dma_off[r], &sm.v[b][blk][c0][0]);
     }
   };
+  auto issue = [&](int t, int b, int e) { issue_for(kend, kvh, tile0 + t, b, e); };
 
   const float sl2 = a.scale * 1.4426950408889634f;
   f32x16_t o[4];
@@ -452,12 +576,31 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const ItemMet
   // t+2 once added) in 4-bit fields.
   const bool late = wave >= 4;
   int e2 = 0, bq = 0;
-  auto step = [&](int t, f32x16_t(&cur)[2], f32x16_t(&nxt)[2]) {
-    const int bc = t & 3;
-    const int bn = (t + 1) & 3;
-    const int bs = (t + 2) & 3;
+  auto step = [&](auto with_scores, int t, f32x16_t(&cur)[2], f32x16_t(&nxt)[2]) {
+    constexpr bool kScores = decltype(with_scores)::value;
+    const int bc = (tb + t) & 3;
+    const int bn = (tb + t + 1) & 3;
+    const int bs = (tb + t + 2) & 3;
     bq |= bad_mask(e2) << 8;  // (read e2 before the tile loads go out)
-    if (t + 2 < ntiles) issue(t + 2, bs, e2);
+    if (t + 2 < ntiles) {
+      issue(t + 2, bs, e2);
+    } else if (has_next && t + 2 - ntiles == next_pre) {
+      // the next item's tile next_pre into the buffer this item's tile t + 2
+      // would take: its last readers (tile t - 2) passed barrier t - 1
+      next = meta_of(a, nraw);
+      const int kend_n = item_kend<G>(a, next);
+      if (kend_n > 0) {
+        issue_for(kend_n, next.kvh, next_pre, bs, next_pre == 0 ? next.e0 : next.e1);
+        ++next_pre;
+      }
+    }
+    if (!kScores && has_next) {
+      // the last step: no score products, so the query registers are free
+      // for the next item's rows
+      next = meta_of(a, nraw);
+      load_query<G, CASCADE>(a, next, qf);
+      next_q = true;
+    }
     e2 = entries(t + 3);
     const int bad = bq & 15;
     // cur[u][4i+j] is the raw score of key t*64 + 32u + 8i + 4hi + j for this
@@ -521,17 +664,21 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const ItemMet
                                 sm.k[bn][2 * u + (n >> 4)][ch][(n & 15) ^ (4 * (ch & 3))]);
     };
     bf16x8_t kq[4];
-    kq[0] = kread(0);
-    kq[1] = kread(1);
-    kq[2] = kread(2);
+    if constexpr (kScores) {
+      kq[0] = kread(0);
+      kq[1] = kread(1);
+      kq[2] = kread(2);
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      if (i + 3 < 16) kq[(i + 3) % 4] = kread(i + 3);
       const int u = i >> 3, ks = i & 7;
-      if (ks == 0)
+      if constexpr (kScores) {
+        if (i + 3 < 16) kq[(i + 3) % 4] = kread(i + 3);
+        if (ks == 0)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) nxt[u][r] = 0.f;
-      nxt[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[i % 4], qf[ks], nxt[u], 0, 0, 0);
+          for (int r = 0; r < 16; ++r) nxt[u][r] = 0.f;
+        nxt[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[i % 4], qf[ks], nxt[u], 0, 0, 0);
+      }
       const int r = 2 * (i & 7);
       const float p0 = fast_exp2(fmaf(cur[u][r], sl2, moff));
       const float p1 = fast_exp2(fmaf(cur[u][r + 1], sl2, moff));
@@ -540,7 +687,10 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const ItemMet
       __builtin_amdgcn_sched_barrier(0);
     }
     lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    if (late) {
+    // (the last step has no barrier: what it would publish -- the next
+    // item's first tiles -- the next item's prologue waits for, and every
+    // buffer the next item refills was last read before barrier t - 1)
+    if (kScores && late) {
       // this wave's loads of tile t+2 (and the entries of tile t+3) have
       // landed; the barrier publishes them
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -564,33 +714,42 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const ItemMet
       __builtin_amdgcn_sched_barrier(0);
     }
     bq >>= 4;
-    if (!late) {
+    if (kScores && !late) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     }
   };
 
-  // the previous item's last V reads (waves 4-7 read after the final barrier)
-  // are done before the first loads of this one refill buffers 0 and 1
-  __syncthreads();
+  // Tiles 0 and 1 go to buffers tb & 3 and (tb + 1) & 3, which the previous
+  // item's last two tiles (the only ones it may still read after its final
+  // barrier) do not use; the barrier below orders everything after that.
   if (ntiles > 0) {
     const int e0 = CASCADE ? entries(0) : im.e0;
-    issue(0, 0, e0);
+    if (pipe.pre < 1) issue(0, tb & 3, e0);
     bq = bad_mask(e0);
     const int e1 = CASCADE ? entries(1) : im.e1;
-    if (ntiles > 1) issue(1, 1, e1);
+    if (pipe.pre < 2 && ntiles > 1) issue(1, (tb + 1) & 3, e1);
     bq |= bad_mask(e1) << 4;
-    e2 = entries(2);
+    e2 = CASCADE ? entries(2) : im.e2;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     f32x16_t sa[2], sb[2];
-    scores(0, sa);
-    for (int t = 0; t < ntiles; ++t) {
-      step(t, sa, sb);
+    scores(tb & 3, sa);
+    // the next item's record, loaded beside this item's third tile
+    if (has_next) nraw = load_rec(a, next_idx);
+    for (int t = 0; t + 1 < ntiles; ++t) {
+      step(std::true_type{}, t, sa, sb);
       sa[0] = sb[0];
       sa[1] = sb[1];
     }
+    step(std::false_type{}, ntiles - 1, sa, sb);
+  } else if (has_next) {
+    nraw = load_rec(a, next_idx);
   }
+  if (has_next) next = meta_of(a, nraw);
+  pipe.tb = tb + max(ntiles, 0);
+  pipe.pre = next_pre;
+  pipe.q_ready = next_q;
 
   // this lane summed 32 of each tile's 64 keys; its partner lane^32 the rest
   const auto ls = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum),
@@ -633,32 +792,29 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const ItemMet
   }
 }
 
-// The metadata and first table entries of work-list item `idx`, loaded
-// directly (a workgroup's first item).
-__device__ __forceinline__ ItemMeta load_item_meta(const PrefillArgs& a, int idx) {
-  const int2 w = prefill_items(a.work)[idx];
-  ItemMeta im;
-  im.seq = __builtin_amdgcn_readfirstlane(w.x);
-  const int y = __builtin_amdgcn_readfirstlane(w.y);
-  im.qtile = y / a.num_kv_heads;
-  im.kvh = y - im.qtile * a.num_kv_heads;
-  im.lo_row = __builtin_amdgcn_readfirstlane(a.cu_seqlens[im.seq]);
-  im.len = __builtin_amdgcn_readfirstlane(a.cu_seqlens[im.seq + 1]) - im.lo_row;
-  im.c = __builtin_amdgcn_readfirstlane(a.context_offsets[im.seq]);
-  const int lane = threadIdx.x & 63;
-  const int32_t* table = a.block_tables + (int64_t)im.seq * a.max_blocks_per_seq;
-  im.e0 = table[min(lane & 3, a.max_blocks_per_seq - 1)];
-  im.e1 = table[min(4 + (lane & 3), a.max_blocks_per_seq - 1)];
-  return im;
-}
-
-// Persistent workgroups walk the longest-first list.
+// Persistent workgroups, one per resident slot, walk the longest-first list
+// in snake order (workgroup i takes ranks i, 2G-1-i, 2G+i, ... for G
+// workgroups), which pairs long items with short ones, each item's start-up
+// overlapped with the end of the one before.
 template <int G>
 __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a) {
   __shared__ PrefillShared sm;
   const int total = a.work[0];
-  for (int it = blockIdx.x; it < total; it += gridDim.x)
-    prefill_item<G, false>(a, load_item_meta(a, it), sm);
+  const int nwg = gridDim.x, wg = blockIdx.x;
+  auto rank = [&](int k) { return k * nwg + ((k & 1) ? nwg - 1 - wg : wg); };
+  if (rank(0) >= total) return;
+  PipeState ps;
+  ps.tb = 0;
+  ps.pre = 0;
+  ps.q_ready = false;
+  ItemMeta cur = meta_of(a, load_rec(a, rank(0)));
+  for (int k = 0;; ++k) {
+    const int nidx = rank(k + 1);  // ranks grow with k: past the end, done
+    ItemMeta next;
+    prefill_item<G, false>(a, cur, sm, ps, nidx < total ? nidx : -1, next);
+    if (nidx >= total) break;
+    cur = next;
+  }
 }
 
 // Common-prefix pass: item (split, row tile, kv head) = (x, y, z).
@@ -669,7 +825,12 @@ __global__ __launch_bounds__(kPrefillThreads) void cascade_prefix_kernel(Prefill
   im.seq = blockIdx.x;
   im.qtile = blockIdx.y;
   im.kvh = blockIdx.z;
-  prefill_item<G, true>(a, im, sm);
+  PipeState ps;
+  ps.tb = 0;
+  ps.pre = 0;
+  ps.q_ready = false;
+  ItemMeta none;
+  prefill_item<G, true>(a, im, sm, ps, -1, none);
 }
 
 static int prefill_cus() {
@@ -701,9 +862,9 @@ static hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t stream) {
     per_cu = nb;
     per_cu_cache.store(nb, std::memory_order_relaxed);
   }
-  // twice the resident workgroups: the dispatcher hands a freed CU the next
-  // one (tuning override PA_PREFILL_GRID, e.g. to give each workgroup many items)
-  int64_t want = (int64_t)2 * per_cu * prefill_cus();
+  // one workgroup per resident slot, each walking its share of the list
+  // (tuning override PA_PREFILL_GRID)
+  int64_t want = (int64_t)per_cu * prefill_cus();
   const char* eg = getenv("PA_PREFILL_GRID");
   if (eg && *eg && atoi(eg) >= 1) want = atoi(eg);
   const int gx = (int)std::max<int64_t>(1, std::min<int64_t>(a.work_cap, want));

@@ -178,14 +178,17 @@ def test_varlen_rows_path(gpu, dtype, d, hq, hkv):
     assert err <= tol, err
 
 
-@pytest.mark.parametrize("grid", ["1", "3", "17"])
-def test_prefill_many_items_per_workgroup(gpu, monkeypatch, grid):
-    """Persistent workgroups run several items each, reading each next item's
-    metadata during the current one: same output, bit for bit, as one item
-    per workgroup, and parity with the oracle."""
+@pytest.mark.parametrize("grid,hq,hkv", [("1", 32, 8), ("3", 32, 8), ("17", 32, 8),
+                                         ("2", 8, 8), ("5", 16, 2)])
+def test_prefill_many_items_per_workgroup(gpu, monkeypatch, grid, hq, hkv):
+    """Persistent workgroups run several items each, the next item's record,
+    first two key tiles and queries loaded during the current one (items of
+    1, 2, 3 and more key tiles back to back): same output, bit for bit, as
+    one item per workgroup, and parity with the oracle."""
     q_lens = [100, 70, 2, 129, 33, 64, 1, 250]
     ctx = [0, 37, 5, 200, 64, 1000, 300, 17]
-    batch = W.varlen_batch(f"many_items_{grid}", 23, q_lens, ctx, 32, 8, 128, "bf16")
+    batch = W.varlen_batch(f"many_items_{grid}_{hq}_{hkv}", 23, q_lens, ctx, hq, hkv, 128,
+                           "bf16")
     db, out = _check(batch)
     ref = out.clone()
     monkeypatch.setenv("PA_PREFILL_GRID", grid)

@@ -24,8 +24,8 @@
 //   * a (block, kv head) tile is 16 * head_dim contiguous elements, so one
 //     wave-wide 16-byte-per-lane load reads 1 KB of consecutive memory; lane l
 //     holds the 16-byte piece (l % LPT) of token row (l / LPT) + k * (64 / LPT);
-//     the single-partition kernel reads the tiles as streaming (non-temporal)
-//     data;
+//     the single-partition and work-list kernels read the tiles as streaming
+//     (non-temporal) data;
 //   * q.k partial sums over a lane's piece are finished with DPP all-reduces
 //     inside the LPT-lane group that holds one token row (LPT = 16 for bf16 at
 //     head_dim 128: exactly one DPP row);
@@ -631,10 +631,13 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
 // 1536 rows of 256-2048 tokens 1185 us against 1295 (6.2 TB/s), 2048 rows of
 // 64 tokens 112 against 115.  The hint costs where many sequences share
 // blocks that the caches would otherwise serve to each of them: 256
-// sequences sharing a 256-token prompt, caches warm, ran 8% slower; in the
-// list kernel, 128 sequences sharing a 4096-token prompt 26% slower, so the
-// list kernel keeps plain loads (a known common prefix is better served by
-// the cascade call, which reads it once).
+// sequences sharing a 256-token prompt, caches warm, ran 8% slower; through
+// the list kernel, 128 sequences sharing a 4096-token prompt 25% slower
+// (353 us against 283) -- a known common prefix is better served by the
+// cascade call, which reads it once (100 us).  The list kernel streams too:
+// the GQA batch of Pareto lengths 77-78 us against 83, the shared-prefix
+// batch 1.445 ms against 1.460 (without the hint, the zero-length loads past
+// a wave's last block alone gained nothing).
 template <bool BF16, int D, int G, bool VARLEN, int NB>
 __global__ __launch_bounds__(256) void decode_direct_kernel(DecodeArgs a) {
   __shared__ DecodeShared<G, D> sm;
@@ -778,7 +781,7 @@ __global__ __launch_bounds__(256) void decode_list_kernel(DecodeArgs a) {
       seq = w.x;
       part = w.y;
     }
-    decode_item<BF16, D, G, VARLEN, NB>(a, seq, part, kvh, sm);
+    decode_item<BF16, D, G, VARLEN, NB, true>(a, seq, part, kvh, sm);
   }
 }
 

@@ -63,11 +63,13 @@
 namespace pa {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float dot_piece(uint4 q, uint4 k, std::true_type /*bf16*/) {
-  float s = 0.f;
-  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.x),
-                                      __builtin_bit_cast(bf16x2_t, k.x), s, false);
+  // the first product with a literal zero accumulator (the compiler would
+  // otherwise clear a register for the accumulating form)
+  float s;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(s) : "v"(q.x), "v"(k.x));
   s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.y),
                                       __builtin_bit_cast(bf16x2_t, k.y), s, false);
   s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.z),
@@ -159,9 +161,13 @@ __device__ __forceinline__ void row_reduce_scatter(float (&x)[NS], int c) {
   rs_step<0xB1, 1, (NS / 8 > 1 ? NS / 8 : 1), NS>(x, c);
 }
 
-// value of lane LANE of the caller's 16-lane row
+// value of lane LANE of the caller's 16-lane row (every lane has a source,
+// so the destination's old value is never kept and needs no clearing)
 template <int LANE>
-__device__ __forceinline__ float row_bcast(float x) { return dpp_f32<0x150 + LANE>(x); }
+__device__ __forceinline__ float row_bcast(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + LANE, 0xF, 0xF, false));
+}
 
 // max / sum over the 4 lanes {c, c+4, c+8, c+12} (mod 16) of a row
 __device__ __forceinline__ float row_max4(float x) {
@@ -417,6 +423,9 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int seq, int pa
       for (int u = 0; u < V; ++u) {
         const float mref = (mu[u] == kNegInf) ? 0.f : mu[u];
         pu[u] = fast_exp2(su[u] - mref);
+        // bf16 values: the weights enter the V products in bf16 (below), so
+        // the sum takes them rounded the same way
+        if constexpr (BF16) pu[u] = round_to_bf16(pu[u]);
         lu[u] += pu[u];
       }
       float p[NS];
@@ -424,14 +433,45 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int seq, int pa
         constexpr int k = decltype(kc)::value;
         p[k] = row_bcast<(NS >= 16 ? k / V : k * R)>(pu[NS >= 16 ? k % V : 0]);
       });
+      if constexpr (BF16) {
+        // O += p V two token rows at a time: the bf16 weights of rows 2jp and
+        // 2jp+1 (exact: rounded above) against the pair (v[2jp][e],
+        // v[2jp+1][e]) gathered by a byte permute, one v_dot2_f32_bf16 per
+        // (head, element) instead of two fp32 FMAs and the widening of v
+        static_assert(NLD % 2 == 0, "token rows are paired");
 #pragma unroll
-      for (int j = 0; j < NLD; ++j)
+        for (int jp = 0; jp < NLD / 2; ++jp) {
+          bf16x2_t pp[G];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          const float v = piece_elem<BF16>(vv[j], e);
+          for (int h = 0; h < G; ++h) {
+            const f32x2_t f = {p[(2 * jp) * G + h], p[(2 * jp + 1) * G + h]};
+            pp[h] = __builtin_convertvector(f, bf16x2_t);
+          }
+          const uint32_t w0[4] = {vv[2 * jp].x, vv[2 * jp].y, vv[2 * jp].z, vv[2 * jp].w};
+          const uint32_t w1[4] = {vv[2 * jp + 1].x, vv[2 * jp + 1].y, vv[2 * jp + 1].z,
+                                  vv[2 * jp + 1].w};
 #pragma unroll
-          for (int h = 0; h < G; ++h) acc[h][e] = fmaf(p[j * G + h], v, acc[h][e]);
+          for (int w = 0; w < EPL / 2; ++w) {
+            // (row 2jp, row 2jp+1) of element 2w, and of element 2w+1
+            const bf16x2_t lo = __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(w1[w], w0[w], 0x05040100u));
+            const bf16x2_t hi = __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(w1[w], w0[w], 0x07060302u));
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+              acc[h][2 * w] = __builtin_amdgcn_fdot2_f32_bf16(pp[h], lo, acc[h][2 * w], false);
+              acc[h][2 * w + 1] = __builtin_amdgcn_fdot2_f32_bf16(pp[h], hi, acc[h][2 * w + 1], false);
+            }
+          }
         }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NLD; ++j)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) {
+            const float v = piece_elem<BF16>(vv[j], e);
+#pragma unroll
+            for (int h = 0; h < G; ++h) acc[h][e] = fmaf(p[j * G + h], v, acc[h][e]);
+          }
+      }
     } else {
       group_sum_n<LPT, NS>(s);
 #pragma unroll

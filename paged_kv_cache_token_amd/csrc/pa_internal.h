@@ -27,6 +27,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   __bf16 b = static_cast<__bf16>(x);
   return __builtin_bit_cast(uint16_t, b);
 }
+// x rounded to the nearest bf16, as fp32 (exact in either format)
+__device__ __forceinline__ float round_to_bf16(float x) {
+  return __uint_as_float((uint32_t)f32_to_bf16_bits(x) << 16);
+}
 
 // ---------------------------------------------------------------------------
 // wavefront reductions

@@ -50,6 +50,7 @@ KERNEL_SOURCES = {
                "paged_kv_cache_token_amd/csrc/pa_internal.h"],
     "prefill": ["paged_kv_cache_token_amd/csrc/pa_prefill.hip",
                 "paged_kv_cache_token_amd/csrc/pa_internal.h"],
+    # every kernel file: calls running decode and matrix-core kernels together
     "cascade": ["paged_kv_cache_token_amd/csrc/pa_decode.hip",
                 "paged_kv_cache_token_amd/csrc/pa_prefill.hip",
                 "paged_kv_cache_token_amd/csrc/pa_internal.h"],
@@ -600,7 +601,7 @@ def measure(name: str, args, dev, headline: bool) -> dict:
     if not prefill_only:
         kern_bytes = att_bytes + (wr_bytes if fused else 0)
         achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
-        traffic = traffic_from_profiles(name, "cascade" if cascade else "decode")
+        traffic = traffic_from_profiles(name, "cascade" if (cascade or kind == "prefill") else "decode")
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": traffic}
@@ -649,7 +650,8 @@ def measure(name: str, args, dev, headline: bool) -> dict:
         "write_bytes": wr_bytes,
         "step_bytes": step_bytes,
         "wall_s_timed": round(wall, 4),
-        "kernel_source_hash": kernel_hash("cascade" if cascade else kind),
+        "kernel_source_hash": kernel_hash("prefill" if prefill_only else
+                                          "cascade" if (cascade or kind == "prefill") else "decode"),
         "call_us_p10_p50_p90": [round(float(np.percentile(att_ms, q)) * 1e3, 2)
                                 for q in (10, 50, 90)],
     }

@@ -62,9 +62,6 @@
 
 namespace pa {
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
 __device__ __forceinline__ float dot_piece(uint4 q, uint4 k, std::true_type /*bf16*/) {
   // the first product with a literal zero accumulator (the compiler would
   // otherwise clear a register for the accumulating form)
@@ -216,6 +213,42 @@ struct DecodeShared {
   float ml[kDecodeMaxWaves][G][2];
   float acc[kDecodeMaxWaves][G][D];
 };
+
+// The item's waves have written their (max, sum, accumulator) per head to
+// sm: combine them and write the output row, or the partition's partial.
+template <bool BF16, int D, int G>
+__device__ __forceinline__ void finish_item(const DecodeArgs& a, const DecodeShared<G, D>& sm,
+                                            int seq, int qrow, int kvh, int part, int nparts) {
+  constexpr float kNegInf = -INFINITY;
+  __syncthreads();
+  const int hq = a.num_q_heads;
+  const int nwaves = a.waves;
+  const int64_t row_base = (int64_t)seq * hq + kvh * G;  // (seq, first q head) partial row
+  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+    const int h = idx / D;
+    const int d = idx - h * D;
+    float mx = kNegInf;
+    for (int w = 0; w < nwaves; ++w) mx = fmaxf(mx, sm.ml[w][h][0]);
+    const float mref = (mx == kNegInf) ? 0.f : mx;
+    float lsum = 0.f, asum = 0.f;
+    for (int w = 0; w < nwaves; ++w) {
+      const float wt = fast_exp2(sm.ml[w][h][0] - mref);
+      lsum += wt * sm.ml[w][h][1];
+      asum += wt * sm.acc[w][h][d];
+    }
+    if (nparts == 1 && a.prefix_parts == 0) {
+      store_elem<BF16>(a.out, ((int64_t)qrow * hq + kvh * G + h) * D + d,
+                       lsum > 0.f ? asum / lsum : 0.f);
+    } else {
+      const int64_t pidx = (row_base + h) * a.max_parts + a.prefix_parts + part;
+      a.ws.acc[pidx * D + d] = asum;
+      if (d == 0) {
+        a.ws.ml[pidx * 2 + 0] = mx;
+        a.ws.ml[pidx * 2 + 1] = lsum;
+      }
+    }
+  }
+}
 
 // One work item: partition `part` of sequence `seq`, kv head `kvh`.  NB
 // register buffers per wave: NB - 1 blocks stay in flight while one is
@@ -582,33 +615,262 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int seq, int pa
       }
     }
   }
-  __syncthreads();
+  finish_item<BF16, D, G>(a, sm, seq, qrow, kvh, part, nparts);
+}
 
-  const int64_t row_base = (int64_t)seq * hq + kvh * G;  // (seq, first q head) partial row
-  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
-    const int h = idx / D;
-    const int d = idx - h * D;
-    float mx = kNegInf;
-    for (int w = 0; w < nwaves; ++w) mx = fmaxf(mx, sm.ml[w][h][0]);
-    const float mref = (mx == kNegInf) ? 0.f : mx;
-    float lsum = 0.f, asum = 0.f;
-    for (int w = 0; w < nwaves; ++w) {
-      const float wt = fast_exp2(sm.ml[w][h][0] - mref);
-      lsum += wt * sm.ml[w][h][1];
-      asum += wt * sm.acc[w][h][d];
+// ---------------------------------------------------------------------------
+// Matrix-core item: bf16 at head_dim 128 with g >= 4 query heads per kv head.
+// ---------------------------------------------------------------------------
+// The waves take the partition's blocks as above; the g query heads are the
+// columns (zero queries past g) of two matrix products per 16-token block:
+//   * S = K Q^T with four v_mfma_f32_16x16x32_bf16 (one per 32 dims).  A is
+//     the block's 16 key rows, loaded from HBM straight into the operand
+//     layout: lane l holds key row l % 16, and for product ks the 16-byte
+//     piece 4 ks + l / 16 of that row; B holds the same pieces of query head
+//     l % 16.  (The pairing of operand elements to dims is the same on both
+//     sides, so the sum over dims is exact whatever the hardware's order.)
+//     Lane l ends with the scores of tokens 4 (l / 16) + r, r = 0..3, for
+//     head l % 16;
+//   * O^T += V^T P^T with eight v_mfma_f32_16x16x16_bf16 (one per 16 dims).
+//     B = P^T is that score accumulator itself, turned into bf16
+//     exponentials in place; A = V^T comes from the transposing LDS read of
+//     the block's V tile, which the wave's buffer loads put straight into
+//     LDS (no register staging).  Lane l accumulates dims 16 m + 4 (l / 16) + r
+//     of head l % 16.
+// The softmax keeps one head per lane column: the block maximum per head takes
+// two cross-row swaps, and the exponentials' reference is raised only when
+// some head's block maximum lies more than 2^8 above it (so p < 256: exact in
+// fp32, bf16's relative precision in the products), all heads rescaled then.
+constexpr float kMfmaLazy = 8.f;  // log2 units
+
+// LDS tiles of one block, [token][16-byte chunk] as the HBM->LDS loads
+// write them (1 KiB of four consecutive token rows per wave instruction),
+// with the chunk position XOR-swizzled by the token so the operand reads hit
+// distinct banks: in K, chunk x of token t sits at x ^ t (the 16-byte reads
+// of 16 tokens at one chunk); in V at x ^ 2 (t & 7) (the transposing 8-byte
+// reads of 8 tokens at two adjacent chunks, per 32 lanes).
+__device__ __forceinline__ int ktile_pos(int t, int x) { return t * 16 + (x ^ t); }
+__device__ __forceinline__ int vtile_pos(int t, int x) { return t * 16 + (x ^ (2 * (t & 7))); }
+constexpr int kWaveTileChunks = 592;  // per wave: K tile, V tile, the staged new row (80)
+
+template <int G, bool VARLEN, bool STREAM>
+__device__ __forceinline__ void decode_item_mfma(const DecodeArgs& a, int seq, int part, int kvh,
+                                                 DecodeShared<G, 128>& sm, uint4* tiles) {
+  constexpr int D = 128;
+  constexpr int kRow = D * 2;                  // bytes of one token row of a tile
+  constexpr int kTile = kBlockSize * kRow;     // bytes of one (block, kv head) tile
+  constexpr int kAux = STREAM ? 2 : 0;         // cache policy of the tile loads (2: nt)
+  constexpr float kNegInf = -INFINITY;
+  static_assert(G >= 2 && G <= 16, "query heads per kv head");
+
+  // (opaque to the compiler, so the lane's tile addresses are derived per
+  // item instead of being held in registers across a persistent kernel's items)
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nwaves = a.waves;
+  const int col = lane & 15;  // key row of K; head column of S, P and O
+  const int grp = lane >> 4;  // piece group of K and Q; tokens 4 grp .. 4 grp + 3 of S
+  const int hq = a.num_q_heads;
+  const int hkv = a.num_kv_heads;
+  const int pt = a.part_tokens;
+  const int tok0 = a.key_start + part * pt;
+
+  int tseq = seq;
+  if constexpr (VARLEN) {
+    if (a.table_rows) tseq = a.table_rows[seq];
+  }
+  const int32_t* table = a.block_tables + (int64_t)tseq * a.max_blocks_per_seq + tok0 / kBlockSize;
+  const int row_left = a.max_blocks_per_seq - tok0 / kBlockSize;  // >= 1 for a live item
+  const int my_entry = table[min(wave + nwaves * lane, row_left - 1)];
+  int qrow, ctx;
+  if (!decode_row<VARLEN>(a, seq, qrow, ctx)) return;
+  const int nparts = parts_of(ctx - a.key_start, pt);
+  if (part >= nparts) return;
+
+  // the query pieces of head `col` (zero past g)
+  uint4 qf[4];
+  {
+    const uint4* qb = static_cast<const uint4*>(a.q) +
+                      ((int64_t)qrow * hq + kvh * G + min(col, G - 1)) * (D / 8) + grp;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = qb[4 * ks];
+  }
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) loaded(qf[ks]);
+  loaded((uint32_t)my_entry);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    if (col >= G) qf[ks] = make_uint4(0u, 0u, 0u, 0u);
+
+  const int tok1 = min(ctx, tok0 + pt);
+  const int nblk = tok1 > tok0 ? ceil_div(tok1 - tok0, kBlockSize) : 0;
+  const int nmine = nblk > wave ? ceil_div(nblk - wave, nwaves) : 0;  // <= 64
+
+  // fused step: as in decode_item
+  const int new_pos = a.key_new != nullptr ? a.context_lens[seq] - 1 : -1;
+  const bool fused = new_pos >= 0 && new_pos < ctx && new_pos >= tok0 && new_pos < tok1;
+  const bool store = fused || (new_pos >= ctx && part == nparts - 1);
+  const int new_off = new_pos % kBlockSize;
+  const int new_blk = fused ? (new_pos - tok0) / kBlockSize : -1;
+  // The wave that consumes or stores the new token's row stages it in LDS
+  // behind its tiles, straight from memory: V's 16 chunks at stage[0..16),
+  // K's at stage[16..32) (each load writes 64 chunks, the lanes past the row
+  // zeros; K's lands second).  These are the wave's oldest loads, so the
+  // tile waits cover them.
+  uint4* ktile = tiles;
+  uint4* vtile = tiles + 256;
+  uint4* stage = tiles + 512;
+  const bool stager = (fused && new_blk % nwaves == wave) || (store && wave == 0);
+  if (stager) {
+    const int64_t row = ((int64_t)seq * hkv + kvh) * kRow;
+    dma16(static_cast<const char*>(a.value_new) + row, kRow, lane * 16, stage);
+    dma16(static_cast<const char*>(a.key_new) + row, kRow, lane * 16, stage + 16);
+  }
+
+  f32x4_t o[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) o[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float mref = kNegInf, lsum = 0.f;
+  const float sl2 = a.scale * 1.4426950408889634f;  // scores in log2 units
+  const char* kc = static_cast<const char*>(a.k_cache);
+  const char* vc = static_cast<const char*>(a.v_cache);
+
+  // The wave's i-th block: its physical id (-1: unusable) and the bytes of
+  // its tile that hold keys of the partition (0 past the wave's last block).
+  auto block_of = [&](int i, int& phys, int64_t& tile, int& bytes) {
+    const int raw = __builtin_amdgcn_readlane(my_entry, min(i, nmine - 1));
+    phys = (raw >= 0 && (int64_t)raw < a.num_blocks) ? raw : -1;
+    const int t_base = tok0 + (wave + nwaves * i) * kBlockSize;
+    bytes = (i < nmine && phys >= 0) ? min(kBlockSize, tok1 - t_base) * kRow : 0;
+    tile = ((int64_t)max(phys, 0) * hkv + kvh) * kTile;
+  };
+  // K and V tiles straight into LDS: load j brings token rows 4 j .. 4 j + 3,
+  // lane (grp, col) the chunk landing at position col of row 4 j + grp.
+  // Loads past the valid bytes write zeros without touching memory.
+  auto load_tiles = [&](int64_t tile, int bytes) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = 4 * j + grp;
+      dma16<kAux>(kc + tile, bytes, t * kRow + (col ^ t) * 16, ktile + 64 * j);
+      dma16<kAux>(vc + tile, bytes, t * kRow + (col ^ (2 * (t & 7))) * 16, vtile + 64 * j);
     }
-    if (nparts == 1 && a.prefix_parts == 0) {
-      store_elem<BF16>(a.out, ((int64_t)qrow * hq + kvh * G + h) * D + d,
-                       lsum > 0.f ? asum / lsum : 0.f);
-    } else {
-      const int64_t pidx = (row_base + h) * a.max_parts + a.prefix_parts + part;
-      a.ws.acc[pidx * D + d] = asum;
-      if (d == 0) {
-        a.ws.ml[pidx * 2 + 0] = mx;
-        a.ws.ml[pidx * 2 + 1] = lsum;
+  };
+  // the transposing reads: lane (grp, col = 4 r + q) addresses token
+  // 4 grp + r at dims 16 m + 4 q .. 16 m + 4 q + 3
+  const int tr_t = 4 * grp + (col >> 2);
+  const int tr_q = col & 3;
+
+  // One block per step; the next block's loads go out as soon as this
+  // block's operands have been read from its LDS tiles, so the products and
+  // the softmax overlap the next block's memory latency.
+  if (nmine > 0) {
+    int phys, bytes;
+    int64_t tile;
+    block_of(0, phys, tile, bytes);
+    load_tiles(tile, bytes);
+    for (int i = 0; i < nmine; ++i) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // block i (and the staged row) landed
+      const int t_base = tok0 + (wave + nwaves * i) * kBlockSize;
+      const int nvalid = phys >= 0 ? min(kBlockSize, tok1 - t_base) : 0;  // wave-uniform
+      if (fused && wave + nwaves * i == new_blk && lane < 16) {
+        // the new token's row comes from the inputs, not the cache: over the
+        // landed tiles' row new_off (the wave's LDS accesses run in order)
+        ktile[ktile_pos(new_off, lane)] = stage[16 + lane];
+        vtile[vtile_pos(new_off, lane)] = stage[lane];
       }
+      uint4 kf[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kf[ks] = ktile[ktile_pos(col, 4 * ks + grp)];
+      const char* vb = reinterpret_cast<const char*>(vtile);
+      uint2 vf[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        vf[m] = lds_read_tr(reinterpret_cast<const uint16_t*>(
+            vb + vtile_pos(tr_t, 2 * m + (tr_q >> 1)) * 16 + (tr_q & 1) * 8));
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the tiles are free again
+      block_of(i + 1, phys, tile, bytes);
+      load_tiles(tile, bytes);
+      if (nvalid <= 0) continue;  // an empty block: all its keys drop out
+
+      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[ks]),
+                                                     __builtin_bit_cast(bf16x8_t, qf[ks]), sc, 0, 0, 0);
+      float y[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y[r] = (4 * grp + r < nvalid) ? sc[r] * sl2 : kNegInf;
+      float bm = fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3]));
+      {
+        const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(bm), __float_as_uint(bm),
+                                                        false, false);
+        bm = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
+        const auto z = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm),
+                                                        false, false);
+        bm = fmaxf(__uint_as_float(z[0]), __uint_as_float(z[1]));
+      }
+      // a block with a valid key has a finite maximum in every column, so the
+      // first one always moves the reference off -inf
+      if (__any(bm > mref + kMfmaLazy)) {
+        const float mn = fmaxf(mref, bm);
+        const float al = fast_exp2(mref - mn);
+        lsum *= al;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) o[m] *= al;
+        mref = mn;
+      }
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(y[r] - mref);
+      // the weights enter the products in bf16, so the sum takes them rounded
+      const uint32_t p01 = pack_f32_bf16(p[0], p[1]);
+      const uint32_t p23 = pack_f32_bf16(p[2], p[3]);
+      lsum += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
+      const bf16x4_t pb = __builtin_bit_cast(bf16x4_t, make_uint2(p01, p23));
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        o[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, vf[m]), pb,
+                                                         o[m], 0, 0, 0);
     }
   }
+  // every load has landed (the trailing zero-length ones still write their
+  // LDS tiles; the staged row is read below)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  if (store && wave == 0 && new_pos / kBlockSize < a.max_blocks_per_seq) {
+    const int raw = a.block_tables[(int64_t)tseq * a.max_blocks_per_seq + new_pos / kBlockSize];
+    if (raw >= 0 && (int64_t)raw < a.num_blocks && lane < 32) {
+      // lanes 0-15 the V chunks, 16-31 the K chunks
+      const int64_t dst = (((int64_t)raw * hkv + kvh) * kBlockSize + new_off) * (D / 8) + col;
+      uint4* cache = static_cast<uint4*>(lane < 16 ? a.v_cache_w : a.k_cache_w);
+      cache[dst] = stage[lane];
+    }
+  }
+
+  // sums per head over the four token groups
+  {
+    const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(lsum), __float_as_uint(lsum),
+                                                    false, false);
+    lsum = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+    const auto z = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum),
+                                                    false, false);
+    lsum = __uint_as_float(z[0]) + __uint_as_float(z[1]);
+  }
+
+  __syncthreads();  // every wave is done with its tiles, which sm overlaps
+  if (col < G) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.acc[wave][col][16 * m + 4 * grp + r] = o[m][r];
+    if (grp == 0) {
+      sm.ml[wave][col][0] = mref;
+      sm.ml[wave][col][1] = lsum;
+    }
+  }
+  finish_item<true, D, G>(a, sm, seq, qrow, kvh, part, nparts);
+  __syncthreads();  // sm overlaps the waves' tiles: read before the next item loads
 }
 
 // Merge the partitions of one (sequence, q head): weights 2^(m_p - max m) in
@@ -678,22 +940,58 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
 // the GQA batch of Pareto lengths 77-78 us against 83, the shared-prefix
 // batch 1.445 ms against 1.460 (without the hint, the zero-length loads past
 // a wave's last block alone gained nothing).
-template <bool BF16, int D, int G, bool VARLEN, int NB>
-__global__ __launch_bounds__(256) void decode_direct_kernel(DecodeArgs a) {
-  __shared__ DecodeShared<G, D> sm;
+// One item through the vector-ALU code or the matrix-core code (MF); dyn is
+// the kernel's dynamic LDS, which starts with the waves' V tiles when MF.
+template <bool BF16, int D, int G, bool VARLEN, int NB, bool MF, bool STREAM>
+__device__ __forceinline__ void run_item(const DecodeArgs& a, int seq, int part, int kvh,
+                                         DecodeShared<G, D>& sm, uint4* dyn) {
+  if constexpr (MF) {
+    static_assert(BF16 && D == 128, "matrix-core decode: bf16 at head_dim 128");
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    decode_item_mfma<G, VARLEN, STREAM>(a, seq, part, kvh, sm, dyn + wave * kWaveTileChunks);
+  } else {
+    decode_item<BF16, D, G, VARLEN, NB, STREAM>(a, seq, part, kvh, sm);
+  }
+}
+
+// The item's merge area: a static LDS array for the vector item code; for the
+// matrix-core code the start of the dynamic LDS, over the waves' tiles.
+template <int G, int D, bool MF>
+__device__ __forceinline__ DecodeShared<G, D>& item_shared(uint4* dyn) {
+  if constexpr (MF) {
+    return *reinterpret_cast<DecodeShared<G, D>*>(dyn);
+  } else {
+    __shared__ DecodeShared<G, D> sm;
+    return sm;
+  }
+}
+
+// dynamic LDS of a decode kernel before any plan arrays: per wave, the K and
+// V tiles and the new token's staged row (80 chunks: the second staging load
+// writes 64 chunks from chunk 16); the item's merge area overlaps them
+template <int G, bool MF>
+constexpr size_t tile_lds_bytes(int waves) {
+  return MF ? std::max((size_t)waves * kWaveTileChunks * 16, sizeof(DecodeShared<G, 128>)) : 0;
+}
+
+template <bool BF16, int D, int G, bool VARLEN, int NB, bool MF>
+__global__ __launch_bounds__(256, MF ? 4 : 1) void decode_direct_kernel(DecodeArgs a) {
+  extern __shared__ uint4 dyn_lds[];
   // kv head fastest: the workgroups of one sequence are dispatched together,
   // so no kv head's share of the work is left to the end of the launch
   const int hkv = a.num_kv_heads;
   const int seq = blockIdx.x / hkv;
-  decode_item<BF16, D, G, VARLEN, NB, true>(a, seq, 0, blockIdx.x - seq * hkv, sm);
+  run_item<BF16, D, G, VARLEN, NB, MF, true>(a, seq, 0, blockIdx.x - seq * hkv,
+                                            item_shared<G, D, MF>(dyn_lds), dyn_lds);
 }
 
 // One workgroup per (sequence, kv head, partition); partitions past a
 // sequence's context exit at once.
-template <bool BF16, int D, int G, bool VARLEN, int NB>
-__global__ __launch_bounds__(256) void decode_grid_kernel(DecodeArgs a) {
-  __shared__ DecodeShared<G, D> sm;
-  decode_item<BF16, D, G, VARLEN, NB>(a, blockIdx.x, blockIdx.z, blockIdx.y, sm);
+template <bool BF16, int D, int G, bool VARLEN, int NB, bool MF>
+__global__ __launch_bounds__(256, MF ? 4 : 1) void decode_grid_kernel(DecodeArgs a) {
+  extern __shared__ uint4 dyn_lds[];
+  run_item<BF16, D, G, VARLEN, NB, MF, false>(a, blockIdx.x, blockIdx.z, blockIdx.y,
+                                             item_shared<G, D, MF>(dyn_lds), dyn_lds);
 }
 
 // The work list without a plan launch: each workgroup derives, from the
@@ -788,10 +1086,10 @@ __device__ __forceinline__ int plan_find(const int* ex, int n, int x) {
 }
 
 // Persistent workgroups walk the (sequence, partition) list for kv head blockIdx.y.
-template <bool BF16, int D, int G, bool VARLEN, int NB>
-__global__ __launch_bounds__(256) void decode_list_kernel(DecodeArgs a) {
-  __shared__ DecodeShared<G, D> sm;
-  extern __shared__ int plan_lds[];  // inline plan: ex_full[n], ex_part[n]
+template <bool BF16, int D, int G, bool VARLEN, int NB, bool MF>
+__global__ __launch_bounds__(256, MF ? 4 : 1) void decode_list_kernel(DecodeArgs a) {
+  extern __shared__ uint4 dyn_lds[];  // [tiles (MF)][inline plan: ex_full[n], ex_part[n]]
+  int* plan_lds = reinterpret_cast<int*>(dyn_lds + tile_lds_bytes<G, MF>(a.waves) / 16);
   int total, total_full = 0;
   if (a.inline_plan)
     inline_plan<VARLEN>(a, plan_lds, plan_lds + a.num_seqs, total_full, total);
@@ -821,7 +1119,8 @@ __global__ __launch_bounds__(256) void decode_list_kernel(DecodeArgs a) {
       seq = w.x;
       part = w.y;
     }
-    decode_item<BF16, D, G, VARLEN, NB, true>(a, seq, part, kvh, sm);
+    run_item<BF16, D, G, VARLEN, NB, MF, true>(a, seq, part, kvh, item_shared<G, D, MF>(dyn_lds),
+                                              dyn_lds);
   }
 }
 
@@ -881,14 +1180,15 @@ static int device_cus() {
   return cus;
 }
 
-template <bool BF16, int D, int G, bool VARLEN, int NB>
+template <bool BF16, int D, int G, bool VARLEN, int NB, bool MF>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   const dim3 block(64 * a.waves);
+  const size_t tiles = tile_lds_bytes<G, MF>(a.waves);
   if (a.max_parts - a.prefix_parts <= 1) {
     // one partition per context (or per private part of a cascade decode,
     // whose partials the merge then combines with the prefix's)
-    hipLaunchKernelGGL((decode_direct_kernel<BF16, D, G, VARLEN, NB>),
-                       dim3((unsigned)a.num_seqs * a.num_kv_heads), block, 0, stream, a);
+    hipLaunchKernelGGL((decode_direct_kernel<BF16, D, G, VARLEN, NB, MF>),
+                       dim3((unsigned)a.num_seqs * a.num_kv_heads), block, tiles, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.prefix_parts == 0) return e;
     hipLaunchKernelGGL((decode_merge_kernel<BF16, D, VARLEN>),
@@ -897,8 +1197,8 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   }
   hipError_t err;
   if (a.grid_mode) {
-    hipLaunchKernelGGL((decode_grid_kernel<BF16, D, G, VARLEN, NB>),
-                       dim3(a.num_seqs, a.num_kv_heads, a.max_parts), block, 0, stream, a);
+    hipLaunchKernelGGL((decode_grid_kernel<BF16, D, G, VARLEN, NB, MF>),
+                       dim3(a.num_seqs, a.num_kv_heads, a.max_parts), block, tiles, stream, a);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL((decode_merge_kernel<BF16, D, VARLEN>),
@@ -906,9 +1206,9 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
                        dim3(D), 0, stream, a);
     return hipGetLastError();
   }
-  size_t plan_lds = 0;
+  size_t plan_lds = tiles;
   if (a.inline_plan) {
-    plan_lds = 2 * sizeof(int) * (size_t)a.num_seqs;
+    plan_lds += 2 * sizeof(int) * (size_t)a.num_seqs;
   } else {
     hipLaunchKernelGGL((decode_plan_kernel<VARLEN>), dim3(1), dim3(1024), 0, stream, a);
     err = hipGetLastError();
@@ -921,8 +1221,8 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   if (resident == 0) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &nb, reinterpret_cast<const void*>(&decode_list_kernel<BF16, D, G, VARLEN, NB>),
-            64 * a.waves, 0) != hipSuccess ||
+            &nb, reinterpret_cast<const void*>(&decode_list_kernel<BF16, D, G, VARLEN, NB, MF>),
+            64 * a.waves, tiles) != hipSuccess ||
         nb <= 0)
       nb = 2;
     resident = nb;
@@ -933,7 +1233,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   const int64_t items_bound = (int64_t)a.num_seqs * a.max_parts;
   const int gx = (int)std::max<int64_t>(
       1, std::min<int64_t>(items_bound, (want + a.num_kv_heads - 1) / a.num_kv_heads));
-  hipLaunchKernelGGL((decode_list_kernel<BF16, D, G, VARLEN, NB>),
+  hipLaunchKernelGGL((decode_list_kernel<BF16, D, G, VARLEN, NB, MF>),
                      dim3((unsigned)gx * a.num_kv_heads), block, plan_lds, stream, a);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -946,14 +1246,17 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
 template <bool BF16, int D, int G, bool VARLEN>
 static hipError_t launch_buffers(const DecodeArgs& a, hipStream_t s) {
   if constexpr (BF16 && D == 128) {
+    if constexpr (G >= 4) {
+      if (a.mfma) return launch_decode_t<BF16, D, G, VARLEN, 1, true>(a, s);
+    }
     switch (a.buffers) {
-      case 1: return launch_decode_t<BF16, D, G, VARLEN, 1>(a, s);
-      case 3: return launch_decode_t<BF16, D, G, VARLEN, 3>(a, s);
-      case 4: return launch_decode_t<BF16, D, G, VARLEN, 4>(a, s);
-      default: return launch_decode_t<BF16, D, G, VARLEN, 2>(a, s);
+      case 1: return launch_decode_t<BF16, D, G, VARLEN, 1, false>(a, s);
+      case 3: return launch_decode_t<BF16, D, G, VARLEN, 3, false>(a, s);
+      case 4: return launch_decode_t<BF16, D, G, VARLEN, 4, false>(a, s);
+      default: return launch_decode_t<BF16, D, G, VARLEN, 2, false>(a, s);
     }
   } else {
-    return launch_decode_t<BF16, D, G, VARLEN, 2>(a, s);
+    return launch_decode_t<BF16, D, G, VARLEN, 2, false>(a, s);
   }
 }
 
@@ -1048,6 +1351,11 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t stream) {
   // batch 82 us against 83.6, the 4096-token common prompt 253 against 263,
   // the long shared-prefix batch within 0.5%.
   if (a.buffers == 0) a.buffers = a.max_parts - a.prefix_parts <= 1 ? 2 : 1;
+  // bf16 at head_dim 128 with >= 4 query heads per kv head: the matrix cores
+  // take the score and value products (PA_DECODE_MFMA=0: the vector code)
+  a.mfma = a.dtype == PA_BF16 && a.head_dim == 128 && a.num_q_heads >= 4 * a.num_kv_heads &&
+           env_int("PA_DECODE_MFMA", 1) != 0;
+  if (a.mfma) a.buffers = 1;  // the matrix-core item code overlaps one block ahead itself
   return a.dtype == PA_BF16 ? launch_dim<true>(a, stream) : launch_dim<false>(a, stream);
 }
 

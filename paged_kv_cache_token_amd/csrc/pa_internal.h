@@ -33,6 +33,43 @@ __device__ __forceinline__ float round_to_bf16(float x) {
 }
 
 // ---------------------------------------------------------------------------
+// vector types, LDS and buffer helpers
+// ---------------------------------------------------------------------------
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// two fp32 -> packed bf16, round to nearest even (one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_f32_bf16(float lo, float hi) {
+  const f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+#define PA_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// 16 bytes per lane from a buffer straight into LDS: lane i's chunk (at
+// byte offset voff of the buffer) lands at lds_base + 16 i (lds_base is
+// wave-uniform); a chunk at or past num_records bytes reads as zeros.  AUX:
+// the load's cache-policy bits (2: non-temporal).
+template <int AUX = 0>
+__device__ __forceinline__ void dma16(const void* base, int num_records, int voff, uint4* lds_base) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, num_records, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, PA_LDS(void, lds_base), 16, voff, 0, 0, AUX);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane s supplies the address of 4 consecutive bf16; lane j = 4q + c of the
+// group receives element c of the chunks of lanes q, 4 + q, 8 + q, 12 + q.
+__device__ __forceinline__ uint2 lds_read_tr(const uint16_t* p) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(PA_LDS(i16x4_t, p)));
+}
+
+// ---------------------------------------------------------------------------
 // wavefront reductions
 // ---------------------------------------------------------------------------
 
@@ -172,6 +209,8 @@ struct DecodeArgs {
   int32_t prefix_parts;            // partial slots [0, prefix_parts) of every (seq, q head)
                                    // hold that prefix's partials; this call's partitions
                                    // follow them, and the merge takes all of them
+  int32_t mfma;                    // bf16, head_dim 128, >= 4 q heads per kv head: the
+                                   // matrix-core item code (set at launch)
 };
 
 struct PrefillArgs {

@@ -50,7 +50,6 @@
 
 namespace pa {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kPrefillD = 128;
@@ -239,33 +238,6 @@ struct __attribute__((aligned(16))) PrefillShared {
   uint4 k[4][4][16][16];
   uint4 v[4][4][16][16];
 };
-
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-// two fp32 -> packed bf16, round to nearest even (one v_cvt_pk_bf16_f32)
-__device__ __forceinline__ uint32_t pack_f32_bf16(float lo, float hi) {
-  const f32x2_t f = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
-}
-
-#define PA_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
-
-// 16 bytes per lane from a buffer straight into LDS: lane i's chunk (at
-// byte offset voff of the buffer) lands at lds_base + 16 i (lds_base is
-// wave-uniform); a chunk at or past num_records bytes reads as zeros.
-__device__ __forceinline__ void dma16(const void* base, int num_records, int voff, uint4* lds_base) {
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, num_records, 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, PA_LDS(void, lds_base), 16, voff, 0, 0, 0);
-}
-
-// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
-// lane s supplies the address of 4 consecutive bf16; lane j = 4q + c of the
-// group receives element c of the chunks of lanes q, 4 + q, 8 + q, 12 + q.
-__device__ __forceinline__ uint2 lds_read_tr(const uint16_t* p) {
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(PA_LDS(i16x4_t, p)));
-}
 
 // A prefill work item's metadata, and the table entries of its first three
 // key tiles (one per lane, lane i: block i & 3 of the tile).

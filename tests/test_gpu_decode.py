@@ -318,10 +318,13 @@ def test_inline_plan_equals_plan_kernel(gpu, monkeypatch, name):
     {"PA_DECODE_PARTITION": "256"}, {"PA_DECODE_PARTITION": "1024"},
     {"PA_DECODE_GRID": "1"}, {"PA_DECODE_OVERSUB": "1"},
     {"PA_DECODE_WAVES": "1", "PA_DECODE_PARTITION": "1024"},
+    {"PA_DECODE_MFMA": "0"}, {"PA_DECODE_MFMA": "0", "PA_DECODE_BUFFERS": "1"},
+    {"PA_DECODE_MFMA": "0", "PA_DECODE_GRID": "1"},
 ], ids=lambda e: ",".join(f"{k[10:].lower()}={v}" for k, v in e.items()))
 def test_decode_launch_variants(gpu, monkeypatch, env):
     """Every launch shape the library can pick (waves per workgroup, register
-    buffers, partition length, grid or list) gives oracle parity."""
+    buffers, partition length, grid or list, matrix-core or vector item code
+    for grouped heads) gives oracle parity."""
     for k, v in env.items():
         monkeypatch.setenv(k, v)
     lens = [1, 2, 15, 16, 17, 100, 511, 512, 513, 1024, 1100, 2049]
@@ -371,3 +374,18 @@ def test_decode_list_beyond_inline_plan(gpu):
     lens[7] = 5000
     batch = W.decode_batch("list_2100", 38, lens, 32, 8, 128, "bf16", pool_factor=1.2)
     _check_decode(batch, check_pools=False)
+
+
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (64, 8), (16, 4)])
+def test_decode_matrix_core_and_vector_items(gpu, monkeypatch, hq, hkv):
+    """Grouped heads (g = 4, 8) in bf16 at head_dim 128 run the matrix-core
+    item code; the vector item code (PA_DECODE_MFMA=0) computes the same
+    attention.  Both against the oracle, on ragged contexts with block,
+    partition and single-partition edges, and the fused step's new token at
+    every offset of its block."""
+    lens = [1, 2, 3, 15, 16, 17, 31, 100, 255, 511, 512, 513, 1024, 1100, 2049, 4100]
+    batch = W.decode_batch(f"items_{hq}_{hkv}", 41, lens, hq, hkv, 128, "bf16", pool_factor=1.3)
+    for mf in ("1", "0"):
+        monkeypatch.setenv("PA_DECODE_MFMA", mf)
+        say("PA_DECODE_MFMA", mf)
+        _check_decode(batch)

@@ -1344,6 +1344,18 @@ bool decode_inline_plan(int num_seqs, int waves) {
 hipError_t launch_decode(const DecodeArgs& args, hipStream_t stream) {
   if (args.num_seqs == 0) return hipSuccess;
   DecodeArgs a = args;
+  // bf16 at head_dim 128 with >= 4 query heads per kv head: the matrix cores
+  // take the score and value products (PA_DECODE_MFMA=0: the vector code)
+  a.mfma = a.dtype == PA_BF16 && a.head_dim == 128 && a.num_q_heads >= 4 * a.num_kv_heads &&
+           env_int("PA_DECODE_MFMA", 1) != 0;
+  // Split contexts on the matrix-core code: one wave per item (no cross-wave
+  // merge, items balance across the chip on their own).  Measured against
+  // four: the GQA Pareto batch 63.5 us against 68.3, the 4096-token common
+  // prompt 240 against 284, the long shared-prefix batch 1.391 ms against
+  // 1.426.  A wave holds 64 table entries, so partitions up to 1024 tokens.
+  if (a.mfma && a.max_parts - a.prefix_parts > 1 &&
+      a.part_tokens <= kBlockSize * kMaxEntriesPerWave && env_int("PA_DECODE_WAVES", 0) == 0)
+    a.waves = 1;
   a.inline_plan = decode_inline_plan(a.num_seqs, a.waves) ? 1 : 0;
   // K/V register buffers per wave (bf16, head_dim 128), unless set: two on
   // the single-partition kernel; one on the split kernels, whose item code
@@ -1351,10 +1363,6 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t stream) {
   // batch 82 us against 83.6, the 4096-token common prompt 253 against 263,
   // the long shared-prefix batch within 0.5%.
   if (a.buffers == 0) a.buffers = a.max_parts - a.prefix_parts <= 1 ? 2 : 1;
-  // bf16 at head_dim 128 with >= 4 query heads per kv head: the matrix cores
-  // take the score and value products (PA_DECODE_MFMA=0: the vector code)
-  a.mfma = a.dtype == PA_BF16 && a.head_dim == 128 && a.num_q_heads >= 4 * a.num_kv_heads &&
-           env_int("PA_DECODE_MFMA", 1) != 0;
   if (a.mfma) a.buffers = 1;  // the matrix-core item code overlaps one block ahead itself
   return a.dtype == PA_BF16 ? launch_dim<true>(a, stream) : launch_dim<false>(a, stream);
 }

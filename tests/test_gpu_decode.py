@@ -313,7 +313,7 @@ def test_inline_plan_equals_plan_kernel(gpu, monkeypatch, name):
 # ---- launch-shape variants ----------------------------------------------------
 
 @pytest.mark.parametrize("env", [
-    {"PA_DECODE_WAVES": "1"}, {"PA_DECODE_WAVES": "2"},
+    {"PA_DECODE_WAVES": "1"}, {"PA_DECODE_WAVES": "2"}, {"PA_DECODE_WAVES": "4"},
     {"PA_DECODE_BUFFERS": "1"}, {"PA_DECODE_BUFFERS": "3"}, {"PA_DECODE_BUFFERS": "4"},
     {"PA_DECODE_PARTITION": "256"}, {"PA_DECODE_PARTITION": "1024"},
     {"PA_DECODE_GRID": "1"}, {"PA_DECODE_OVERSUB": "1"},

@@ -62,7 +62,11 @@ def test_mixed_rows_small(gpu):
 
 
 def test_packing_invariance(gpu):
-    """Each sequence's rows are the same whether it is packed with others or alone."""
+    """Each sequence's rows are the same whether it is packed with others or
+    alone: bit for bit for the prefill chunks (one item per query tile,
+    whatever else is packed); a decode row's split over partitions and waves
+    follows the call's shape (its longest context, whether any context is
+    split), so packed and alone it agrees within the bf16 bar."""
     import paged_kv_cache_token_amd as pa
     q_lens = [1, 96, 1, 40]
     ctx = [500, 33, 1200, 0]
@@ -77,7 +81,11 @@ def test_packing_invariance(gpu):
         solo = pa.varlen_prefill(db.q[lo:hi].contiguous(), db.k_cache, db.v_cache, cu, co, bt,
                                  hi - lo, int(batch.context_lens[i]), batch.scale)
         torch.cuda.synchronize()
-        assert torch.equal(solo, packed[lo:hi]), i
+        if hi - lo > 1:
+            assert torch.equal(solo, packed[lo:hi]), i
+        else:
+            err = float((solo.float() - packed[lo:hi].float()).abs().max())
+            assert err <= TOL, (i, err)
 
 
 def test_prefill_rows_match_decode(gpu):

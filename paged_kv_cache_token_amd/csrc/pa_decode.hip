@@ -619,7 +619,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int seq, int pa
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core item: bf16 at head_dim 128 with g >= 4 query heads per kv head.
+// Matrix-core item: bf16 at head_dim 128 (any g up to 16 query heads per kv head).
 // ---------------------------------------------------------------------------
 // The waves take the partition's blocks as above; the g query heads are the
 // columns (zero queries past g) of two matrix products per 16-token block:
@@ -661,7 +661,7 @@ __device__ __forceinline__ void decode_item_mfma(const DecodeArgs& a, int seq, i
   constexpr int kTile = kBlockSize * kRow;     // bytes of one (block, kv head) tile
   constexpr int kAux = STREAM ? 2 : 0;         // cache policy of the tile loads (2: nt)
   constexpr float kNegInf = -INFINITY;
-  static_assert(G >= 2 && G <= 16, "query heads per kv head");
+  static_assert(G >= 1 && G <= 16, "query heads per kv head");
 
   // (opaque to the compiler, so the lane's tile addresses are derived per
   // item instead of being held in registers across a persistent kernel's items)
@@ -1246,9 +1246,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
 template <bool BF16, int D, int G, bool VARLEN>
 static hipError_t launch_buffers(const DecodeArgs& a, hipStream_t s) {
   if constexpr (BF16 && D == 128) {
-    if constexpr (G >= 4) {
-      if (a.mfma) return launch_decode_t<BF16, D, G, VARLEN, 1, true>(a, s);
-    }
+    if (a.mfma) return launch_decode_t<BF16, D, G, VARLEN, 1, true>(a, s);
     switch (a.buffers) {
       case 1: return launch_decode_t<BF16, D, G, VARLEN, 1, false>(a, s);
       case 3: return launch_decode_t<BF16, D, G, VARLEN, 3, false>(a, s);
@@ -1344,10 +1342,12 @@ bool decode_inline_plan(int num_seqs, int waves) {
 hipError_t launch_decode(const DecodeArgs& args, hipStream_t stream) {
   if (args.num_seqs == 0) return hipSuccess;
   DecodeArgs a = args;
-  // bf16 at head_dim 128 with >= 4 query heads per kv head: the matrix cores
-  // take the score and value products (PA_DECODE_MFMA=0: the vector code)
-  a.mfma = a.dtype == PA_BF16 && a.head_dim == 128 && a.num_q_heads >= 4 * a.num_kv_heads &&
-           env_int("PA_DECODE_MFMA", 1) != 0;
+  // bf16 at head_dim 128: the matrix cores take the score and value products
+  // (PA_DECODE_MFMA=0: the vector code).  Measured against the vector code on
+  // one box: the LLaMA-2-shaped step (g = 1) 49.6 us against 50.8, the GQA
+  // batch (g = 4) 68.5 against 75.5, the same lengths at g = 2 55.9 against
+  // 60.1, long and short g = 1 batches 0.5-1.7% faster.
+  a.mfma = a.dtype == PA_BF16 && a.head_dim == 128 && env_int("PA_DECODE_MFMA", 1) != 0;
   // Split contexts on the matrix-core code: one wave per item (no cross-wave
   // merge, items balance across the chip on their own).  Measured against
   // four: the GQA Pareto batch 63.5 us against 68.3, the 4096-token common

@@ -209,8 +209,8 @@ struct DecodeArgs {
   int32_t prefix_parts;            // partial slots [0, prefix_parts) of every (seq, q head)
                                    // hold that prefix's partials; this call's partitions
                                    // follow them, and the merge takes all of them
-  int32_t mfma;                    // bf16, head_dim 128, >= 4 q heads per kv head: the
-                                   // matrix-core item code (set at launch)
+  int32_t mfma;                    // bf16 at head_dim 128: the matrix-core item code
+                                   // (set at launch)
 };
 
 struct PrefillArgs {

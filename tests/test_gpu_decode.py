@@ -323,8 +323,8 @@ def test_inline_plan_equals_plan_kernel(gpu, monkeypatch, name):
 ], ids=lambda e: ",".join(f"{k[10:].lower()}={v}" for k, v in e.items()))
 def test_decode_launch_variants(gpu, monkeypatch, env):
     """Every launch shape the library can pick (waves per workgroup, register
-    buffers, partition length, grid or list, matrix-core or vector item code
-    for grouped heads) gives oracle parity."""
+    buffers, partition length, grid or list, matrix-core or vector item code)
+    gives oracle parity."""
     for k, v in env.items():
         monkeypatch.setenv(k, v)
     lens = [1, 2, 15, 16, 17, 100, 511, 512, 513, 1024, 1100, 2049]
@@ -376,11 +376,10 @@ def test_decode_list_beyond_inline_plan(gpu):
     _check_decode(batch, check_pools=False)
 
 
-@pytest.mark.parametrize("hq,hkv", [(32, 8), (64, 8), (16, 4)])
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (64, 8), (16, 4), (8, 8), (16, 8)])
 def test_decode_matrix_core_and_vector_items(gpu, monkeypatch, hq, hkv):
-    """Grouped heads (g = 4, 8) in bf16 at head_dim 128 run the matrix-core
-    item code; the vector item code (PA_DECODE_MFMA=0) computes the same
-    attention.  Both against the oracle, on ragged contexts with block,
+    """bf16 at head_dim 128 runs the matrix-core item code (g = 1 to 8 here);
+    the vector item code (PA_DECODE_MFMA=0) computes the same attention.  Both against the oracle, on ragged contexts with block,
     partition and single-partition edges, and the fused step's new token at
     every offset of its block."""
     lens = [1, 2, 3, 15, 16, 17, 31, 100, 255, 511, 512, 513, 1024, 1100, 2049, 4100]

@@ -18,20 +18,24 @@
 //   * the waves take the partition's 16-token blocks round-robin.  A wave
 //     reads its block-table entries once (one entry per lane, issued together
 //     with the context length and the query) and broadcasts them with
-//     readlane, so the only vector loads in its loop are K and V; it keeps the
-//     next block's K and V in flight while it computes the current one (two
-//     register buffers, alternating);
+//     readlane, so the only vector loads in its loop are K and V;
 //   * a (block, kv head) tile is 16 * head_dim contiguous elements, so one
-//     wave-wide 16-byte-per-lane load reads 1 KB of consecutive memory; lane l
-//     holds the 16-byte piece (l % LPT) of token row (l / LPT) + k * (64 / LPT);
-//     the single-partition and work-list kernels read the tiles as streaming
+//     wave-wide 16-byte-per-lane load reads 1 KB of consecutive memory; the
+//     single-partition and work-list kernels read the tiles as streaming
 //     (non-temporal) data;
-//   * q.k partial sums over a lane's piece are finished with DPP all-reduces
-//     inside the LPT-lane group that holds one token row (LPT = 16 for bf16 at
-//     head_dim 128: exactly one DPP row);
-//   * each lane group keeps its own running (max, sum, accumulator) over the
-//     token rows it holds; groups are merged at the end of the item, across the
-//     wave with lane exchanges, then across the 4 waves in LDS;
+//   * bf16 at head_dim 128 runs the matrix-core item code (decode_item_mfma):
+//     the tiles go HBM -> LDS and the block's score and value products are
+//     two matrix products with the g query heads as columns; the next block's
+//     loads are issued as soon as the current block's operands are read;
+//   * fp32 and head_dim 64 run the vector item code (decode_item): lane l
+//     holds the 16-byte piece (l % LPT) of token row (l / LPT) + k * (64 / LPT)
+//     in registers (the next block's K and V in flight while the current one
+//     is computed); q.k partial sums over a lane's piece are finished with DPP
+//     all-reduces inside the LPT-lane group that holds one token row; each
+//     lane group keeps its own running (max, sum, accumulator) over the token
+//     rows it holds, merged at the end of the item across the wave with lane
+//     exchanges;
+//   * the waves of an item are merged in LDS;
 //   * an item whose sequence has one partition writes `out` directly.  Otherwise
 //     it stores (max, sum, accumulator) in the workspace, and a merge kernel
 //     combines the sequence's partitions in ascending order and writes `out`
@@ -1357,11 +1361,12 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t stream) {
       a.part_tokens <= kBlockSize * kMaxEntriesPerWave && env_int("PA_DECODE_WAVES", 0) == 0)
     a.waves = 1;
   a.inline_plan = decode_inline_plan(a.num_seqs, a.waves) ? 1 : 0;
-  // K/V register buffers per wave (bf16, head_dim 128), unless set: two on
-  // the single-partition kernel; one on the split kernels, whose item code
-  // then fits 128 VGPRs (4 waves per SIMD instead of 3): the Pareto GQA
-  // batch 82 us against 83.6, the 4096-token common prompt 253 against 263,
-  // the long shared-prefix batch within 0.5%.
+  // K/V register buffers per wave of the vector item code (bf16 at head_dim
+  // 128 with PA_DECODE_MFMA=0), unless set: two on the single-partition
+  // kernel; one on the split kernels, whose item code then fits 128 VGPRs (4
+  // waves per SIMD instead of 3): the Pareto GQA batch 82 us against 83.6,
+  // the 4096-token common prompt 253 against 263, the long shared-prefix
+  // batch within 0.5%.
   if (a.buffers == 0) a.buffers = a.max_parts - a.prefix_parts <= 1 ? 2 : 1;
   if (a.mfma) a.buffers = 1;  // the matrix-core item code overlaps one block ahead itself
   return a.dtype == PA_BF16 ? launch_dim<true>(a, stream) : launch_dim<false>(a, stream);

@@ -33,6 +33,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -57,10 +58,18 @@ KERNEL_SOURCES = {
 }
 
 
+def _code_only(text: str) -> str:
+    """A kernel source with its comments and layout removed: the counters
+    stored under profiles/ stay valid across edits that change no code."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_hash(kind: str) -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES[kind]:
-        h.update(open(os.path.join(ROOT, p), "rb").read())
+        h.update(_code_only(open(os.path.join(ROOT, p), encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -877,12 +877,86 @@ __device__ __forceinline__ void decode_item_mfma(const DecodeArgs& a, int seq, i
   __syncthreads();  // sm overlaps the waves' tiles: read before the next item loads
 }
 
-// Merge the partitions of one (sequence, q head): weights 2^(m_p - max m) in
-// ascending partition order.  Runs after the partition kernel on the same
-// stream; the kernel boundary makes the partials visible.
+// Merge the partitions of one (sequence, q head): weights 2^(m_p - max m), the
+// accumulators summed in ascending partition order.  Runs after the partition
+// kernel on the same stream; the kernel boundary makes the partials visible.
+// The loads go out in few dependent rounds: the first B accumulators together
+// with every (max, sum) pair (thread t holds partition t's), the weights
+// through LDS, then the accumulators B partitions at a time (a cascade call's
+// 33 partials: two rounds with B = 32, not the ten of one pass per value in
+// batches of 8).  B = 8 when there are at most 8 partials.
+constexpr int kMergeLdsParts = 1024;  // partitions whose weights LDS holds
+
+template <int B, bool BF16, int D>
+__device__ __forceinline__ void merge_row(const DecodeArgs& a, int nparts, int64_t prow,
+                                          int64_t out_idx, float (&wts)[kMergeLdsParts],
+                                          float (&red)[2][D / 64]) {
+  constexpr float kNegInf = -INFINITY;
+  constexpr int kWaves = D / 64;
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const float* ml = a.ws.ml + prow * 2;
+  const float* pacc = a.ws.acc + prow * D + t;
+
+  // first round (indices past the last partition are clamped, values unused)
+  float av[B];
+#pragma unroll
+  for (int j = 0; j < B; ++j) av[j] = pacc[(int64_t)min(j, nparts - 1) * D];
+  float m_own = kNegInf, l_own = 0.f;
+  if (t < nparts) {
+    m_own = ml[2 * t];
+    l_own = ml[2 * t + 1];
+  }
+  float mloc = m_own;
+  for (int p = t + D; p < nparts; p += D) mloc = fmaxf(mloc, ml[2 * p]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
+  if (lane == 0) red[0][wave] = mloc;
+  __syncthreads();
+  float mx = red[0][0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, red[0][w]);
+  const float mref = (mx == kNegInf) ? 0.f : mx;
+  // each partition's weight (into LDS) and the weighted sums: a thread's
+  // partitions ascending, then across lanes and waves in a fixed order
+  float lloc = 0.f;
+  if (t < nparts) {
+    const float wt = fast_exp2(m_own - mref);
+    if (t < kMergeLdsParts) wts[t] = wt;
+    lloc = wt * l_own;
+  }
+  for (int p = t + D; p < nparts; p += D) {
+    const float wt = fast_exp2(ml[2 * p] - mref);
+    if (p < kMergeLdsParts) wts[p] = wt;
+    lloc += wt * ml[2 * p + 1];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) lloc += __shfl_xor(lloc, off);
+  if (lane == 0) red[1][wave] = lloc;
+  __syncthreads();
+  float lsum = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) lsum += red[1][w];
+
+  auto weight = [&](int q) { return q < kMergeLdsParts ? wts[q] : fast_exp2(ml[2 * q] - mref); };
+  float asum = 0.f;
+#pragma unroll
+  for (int j = 0; j < B; ++j)
+    if (j < nparts) asum += weight(j) * av[j];
+  for (int p = B; p < nparts; p += B) {
+#pragma unroll
+    for (int j = 0; j < B; ++j) av[j] = pacc[(int64_t)min(p + j, nparts - 1) * D];
+#pragma unroll
+    for (int j = 0; j < B; ++j)
+      if (p + j < nparts) asum += weight(p + j) * av[j];
+  }
+  store_elem<BF16>(a.out, out_idx, lsum > 0.f ? asum / lsum : 0.f);
+}
+
 template <bool BF16, int D, bool VARLEN>
 __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
-  constexpr float kNegInf = -INFINITY;
+  __shared__ float wts[kMergeLdsParts];
+  __shared__ float red[2][D / 64];
   // one workgroup per (sequence, q head), q head fastest (a 1-D grid: packed
   // calls taken row by row can have more rows than a grid's y extent)
   const int seq = blockIdx.x / a.num_q_heads;
@@ -892,43 +966,12 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
   const int nparts = a.prefix_parts + parts_of(ctx - a.key_start, a.part_tokens);
   if (nparts <= 1) return;
   const int hq = a.num_q_heads;
-  const int d = threadIdx.x;
   const int64_t prow = ((int64_t)seq * hq + h) * a.max_parts;
-  const float* ml = a.ws.ml + prow * 2;
-  const float* pacc = a.ws.acc + prow * D + d;
-  // partials are read U at a time, all loads of a batch issued before any
-  // is used (indices past the last partition are clamped, their values
-  // unused), so the latency is paid once per batch instead of per partition
-  constexpr int U = 8;
-  float mx = kNegInf;
-  for (int p = 0; p < nparts; p += U) {
-    float mv[U];
-#pragma unroll
-    for (int j = 0; j < U; ++j) mv[j] = ml[2 * min(p + j, nparts - 1)];
-#pragma unroll
-    for (int j = 0; j < U; ++j) mx = fmaxf(mx, mv[j]);
-  }
-  const float mref = (mx == kNegInf) ? 0.f : mx;
-  float lsum = 0.f, asum = 0.f;
-  for (int p = 0; p < nparts; p += U) {
-    float mv[U], lv[U], av[U];
-#pragma unroll
-    for (int j = 0; j < U; ++j) {
-      const int q = min(p + j, nparts - 1);
-      mv[j] = ml[2 * q];
-      lv[j] = ml[2 * q + 1];
-      av[j] = pacc[(int64_t)q * D];
-    }
-#pragma unroll
-    for (int j = 0; j < U; ++j) {
-      if (p + j < nparts) {
-        const float wt = fast_exp2(mv[j] - mref);
-        lsum += wt * lv[j];
-        asum += wt * av[j];
-      }
-    }
-  }
-  store_elem<BF16>(a.out, ((int64_t)qrow * hq + h) * D + d, lsum > 0.f ? asum / lsum : 0.f);
+  const int64_t out_idx = ((int64_t)qrow * hq + h) * D + threadIdx.x;
+  if (nparts <= 8)
+    merge_row<8, BF16, D>(a, nparts, prow, out_idx, wts, red);
+  else
+    merge_row<32, BF16, D>(a, nparts, prow, out_idx, wts, red);
 }
 
 // Every context fits one partition: one workgroup per (sequence, kv head).

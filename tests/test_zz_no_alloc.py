@@ -3,7 +3,8 @@ fixed per-GPU scratch instead of a caller workspace (for callers that cannot
 allocate).  Called through the C ABI (the binding marshals pointers only) and
 compared with pa_decode on the same inputs, bit for bit, and with the oracle
 at the bf16 bar, on two calls in a row, the second smaller: the scratch keeps
-the first call's contents, which the second must not read."""
+the first call's contents, which the second must not read; and captured in a
+HIP graph, replayed."""
 import sys
 
 import numpy as np
@@ -58,6 +59,48 @@ def test_noalloc_fp32_and_single_partition(gpu):
     _one(W.decode_batch("noalloc_f32", 73, [1, 16, 17, 700, 1500], 8, 8, 64, "f32",
                         pool_factor=1.3))
     _one(W.llama2_decode())
+
+
+def test_noalloc_in_a_graph(gpu):
+    """The callers it is for: a captured pa_decode_noalloc (work list, split
+    items and merge on the library's scratch) replayed four times with eager
+    work between, every replay equal to the eager call bit for bit and to
+    the oracle within the bar."""
+    import paged_kv_cache_token_amd as pa
+    from device_batch import DeviceBatch
+    batch = W.decode_batch("noalloc_graph", 74, [1, 17, 513, 1100, 2049, 4096, 300] * 4, 32, 8,
+                           128, "bf16", pool_factor=1.2)
+    say("noalloc graph", batch.name)
+    db = DeviceBatch(batch)
+    db.write_new()
+    out = torch.empty_like(db.q)
+
+    def run():
+        pa.decode_noalloc(db.q, db.k_cache, db.v_cache, db.block_tables, db.context_lens,
+                          batch.max_context_len, batch.scale, out=out)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    hs = host_state(batch)
+    want = expected(batch, hs)
+    for r in range(4):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {r} differs from the eager call"
+        err = float(np.abs(out.float().cpu().numpy().astype(np.float64) - want).max())
+        say("replay", r, "max abs err", err)
+        assert err <= TOL[batch.dtype], err
+        torch.randn(1 << 20, device="cuda").sum().item()
 
 
 def test_noalloc_refuses_beyond_scratch(gpu):

@@ -45,6 +45,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "pa_launch.h"
 
@@ -254,10 +255,34 @@ struct RecRaw {
   int c, e0, e1, e2;
 };
 
-__device__ __forceinline__ RecRaw load_rec(const PrefillArgs& a, int idx) {
-  const int32_t* r = prefill_rec(a.work, idx);
+// A workgroup's own items when it builds the work list itself: its k-th item
+// (rank k of the snake order) in entry k, the same fields as words 0..4 of a
+// record in the workspace list.
+constexpr int kListCap = 256;
+struct ItemList {
+  int4 m[kListCap];
+  int c[kListCap];
+};
+
+// Item idx's record: from the workspace list (idx is the item's rank), or,
+// when the workgroup built its own list (INL), entry idx of `list` (in LDS),
+// whose table entries are read from the block table here.
+template <bool INL>
+__device__ __forceinline__ RecRaw load_rec(const PrefillArgs& a, int idx, const ItemList* list) {
   const int lane = threadIdx.x & 63;
   RecRaw x;
+  if constexpr (INL) {
+    const auto* e = PA_LDS(const int, &list->m[idx]);
+    x.m = make_int4(e[0], e[1], e[2], e[3]);
+    x.c = *PA_LDS(const int, &list->c[idx]);
+    const int32_t* table = a.block_tables + (int64_t)x.m.x * a.max_blocks_per_seq;
+    const int last = a.max_blocks_per_seq - 1;
+    x.e0 = table[min(lane & 3, last)];
+    x.e1 = table[min(4 + (lane & 3), last)];
+    x.e2 = table[min(8 + (lane & 3), last)];
+    return x;
+  }
+  const int32_t* r = prefill_rec(a.work, idx);
   x.m = *reinterpret_cast<const int4*>(r);
   x.c = r[4];
   x.e0 = r[8 + (lane & 3)];
@@ -348,16 +373,17 @@ struct PipeState {
 // unnormalised partials instead of the output.
 //
 // Items run back to back in a workgroup overlap their start-up with the end
-// of the previous item: given the next item's index, the running one loads
-// its record with its own first key tile, starts the next item's first two
+// of the previous item: given the next item's index (its rank in the
+// workspace list, or its entry in the workgroup's own `list`), the running one
+// loads its record with its own first key tile, starts the next item's first two
 // key tiles into the LDS buffers its own last two steps leave free, and loads
 // the next item's queries during its own last step (which skips the discarded
 // score products that would read them).  On return `next` holds the next
 // item and `pipe` what was started for it.
-template <int G, bool CASCADE>
+template <int G, bool CASCADE, bool INL = false>
 __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const ItemMeta& im,
                                              PrefillShared& sm, PipeState& pipe, int next_idx,
-                                             ItemMeta& next) {
+                                             const ItemList* list, ItemMeta& next) {
   const int seq = im.seq, qtile = im.qtile, kvh = im.kvh;
   constexpr int D = kPrefillD;
   constexpr int BMT = kPrefillRows / G;  // query tokens per item
@@ -708,7 +734,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const ItemMet
     f32x16_t sa[2], sb[2];
     scores(tb & 3, sa);
     // the next item's record, loaded beside this item's third tile
-    if (has_next) nraw = load_rec(a, next_idx);
+    if (has_next) nraw = load_rec<INL>(a, next_idx, list);
     for (int t = 0; t + 1 < ntiles; ++t) {
       step(std::true_type{}, t, sa, sb);
       sa[0] = sb[0];
@@ -716,7 +742,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const ItemMet
     }
     step(std::false_type{}, ntiles - 1, sa, sb);
   } else if (has_next) {
-    nraw = load_rec(a, next_idx);
+    nraw = load_rec<INL>(a, next_idx, list);
   }
   if (has_next) next = meta_of(a, nraw);
   pipe.tb = tb + max(ntiles, 0);
@@ -768,10 +794,181 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const ItemMet
 // in snake order (workgroup i takes ranks i, 2G-1-i, 2G+i, ... for G
 // workgroups), which pairs long items with short ones, each item's start-up
 // overlapped with the end of the one before.
-template <int G>
+// The work list built inside every workgroup (no plan launch): the same
+// (sequence, query tile, kv head) items as the plan kernel lists, ordered by
+// key tiles, most first, and within one count by (sequence, query tile) --
+// a stable counting sort, so every workgroup derives the same order -- of
+// which the workgroup keeps only the items of its own snake ranks, in `list`.
+// Scratch: the tile buffers `w`, before any tile is loaded.  Returns the item
+// count (every thread).  Needs num_seqs <= kInlineMaxSeqs, at most
+// kInlineMaxPairs (sequence, query tile) pairs (more are dropped, as are
+// items past work_cap: the host bounds both) and work_cap <= kListCap x grid.
+constexpr int kInlineMaxSeqs = 4096;   // a pair's sequence takes 12 bits of its word
+constexpr int kInlineMaxPairs = 7168;
+
+__device__ __forceinline__ int inline_scan(int v, int& total, int* wt) {
+  constexpr int NW = kPrefillThreads / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int up = __shfl_up(inc, off);
+    if (lane >= off) inc += up;
+  }
+  if (lane == 63) wt[wave] = inc;
+  __syncthreads();
+  int base = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int x = wt[w];
+    base += w < wave ? x : 0;
+    total += x;
+  }
+  __syncthreads();  // wt is reused by the next scan
+  return base + inc - v;
+}
+
+__device__ int plan_inline(const PrefillArgs& a, int tile_tokens, int* w, ItemList& list) {
+  constexpr int NT = kPrefillThreads, NW = NT / 64;
+  constexpr int B = kSortBuckets;
+  int* cnt = w;                            // [B] pairs per bucket, then first pair
+  int* cw = cnt + B;                       // [NW][B] per-wave counts, then offsets
+  int* scu = cw + NW * B;                  // [n + 1] first packed row of each sequence
+  int* sctx = scu + kInlineMaxSeqs + 1;    // [n] cached tokens
+  int* psq = sctx + kInlineMaxSeqs;        // [pairs] sequence | query tile << 12
+  int* pkey = psq + kInlineMaxPairs;       // [pairs] bucket | rank among its wave's equals << 10
+  int* wt = pkey + kInlineMaxPairs;        // [NW] scan scratch
+  static_assert(kInlineMaxSeqs <= 4096, "sequence index in 12 bits");
+  static_assert((NW + 1) * B + 2 * kInlineMaxSeqs + 1 + 2 * kInlineMaxPairs + NW <=
+                    (int)(sizeof(PrefillShared) / sizeof(int)),
+                "inline plan scratch fits the tile buffers");
+  static_assert(B == 2 * NT, "two buckets per thread");
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int n = a.num_seqs, hkv = a.num_kv_heads;
+  const int maxk = max(0, min(a.max_context_len, a.max_blocks_per_seq * kBlockSize));
+  for (int i = t; i < (NW + 1) * B; i += NT) w[i] = 0;
+
+  // sequences [s0, s0 + C) of this thread: lengths and cached counts into LDS,
+  // and their query tiles (sequences of one row have none)
+  const int C = ceil_div(n, NT);
+  const int s0 = t * C;
+  int mine = 0;
+  for (int j = 0; j < C; ++j) {
+    const int s = s0 + j;
+    if (s >= n) break;
+    const int lo = a.cu_seqlens[s], hi = a.cu_seqlens[s + 1];
+    scu[s] = lo;
+    sctx[s] = a.context_offsets[s];
+    if (s == n - 1) scu[n] = hi;
+    mine += hi - lo >= 2 ? ceil_div(hi - lo, tile_tokens) : 0;
+  }
+  int npairs = 0;
+  int p = inline_scan(mine, npairs, wt);  // barrier: scu complete
+  npairs = min(npairs, kInlineMaxPairs);
+  for (int j = 0; j < C; ++j) {
+    const int s = s0 + j;
+    if (s >= n) break;
+    const int len = scu[s + 1] - scu[s];
+    const int nt = len >= 2 ? ceil_div(len, tile_tokens) : 0;
+    for (int q = 0; q < nt && p < kInlineMaxPairs; ++q, ++p) psq[p] = s | (q << 12);
+  }
+  __syncthreads();
+
+  auto bucket = [&](int s, int q) {
+    const int len = scu[s + 1] - scu[s], c = sctx[s];
+    const int qn = min(tile_tokens, len - q * tile_tokens);
+    const int kend = max(0, min(c + q * tile_tokens + qn, maxk));
+    return min(ceil_div(kend, kKeyTile), B - 1);
+  };
+  for (int i = t; i < npairs; i += NT) {
+    const int b = bucket(psq[i] & 4095, psq[i] >> 12);
+    pkey[i] = b;
+    atomicAdd(&cnt[b], 1);
+  }
+  __syncthreads();
+  // first pair of each bucket, largest bucket first: thread t owns buckets
+  // B-1-2t and B-2-2t
+  {
+    const int b0 = B - 1 - 2 * t, b1 = b0 - 1;
+    const int x0 = cnt[b0], x1 = cnt[b1];
+    int unused;
+    const int off = inline_scan(x0 + x1, unused, wt);
+    cnt[b0] = off;
+    cnt[b1] = off + x0;
+  }
+  // stable rank among equal buckets: wave v walks pairs [v S, (v + 1) S) 64 at
+  // a time; the lanes holding one bucket find each other by ballots over its
+  // bits, and the lowest of them advances the wave's count for that bucket
+  const int S = ceil_div(npairs, NW);
+  {
+    int* mycw = cw + wave * B;
+    const int end = min(npairs, (wave + 1) * S);
+    for (int base = wave * S; base < end; base += 64) {
+      const int i = base + lane;
+      const bool valid = i < end;
+      const int b = valid ? pkey[i] : 0;
+      uint64_t peers = __ballot(valid);
+#pragma unroll
+      for (int bit = 0; bit < 10; ++bit) {
+        const bool on = (b >> bit) & 1;
+        const uint64_t m = __ballot(valid && on);
+        peers &= on ? m : ~m;
+      }
+      const int below = __popcll(peers & ((1ull << lane) - 1ull));
+      const int old = valid ? mycw[b] : 0;
+      if (valid && below == 0) mycw[b] = old + __popcll(peers);
+      if (valid) pkey[i] = b | ((old + below) << 10);
+    }
+  }
+  __syncthreads();
+  // per bucket: the waves' counts -> each wave's first rank
+  for (int b = t; b < B; b += NT) {
+    int pre = 0;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      const int x = cw[v * B + b];
+      cw[v * B + b] = pre;
+      pre += x;
+    }
+  }
+  __syncthreads();
+  // place: pair i's items are pos*hkv + h; keep those of this workgroup's
+  // snake ranks (rank k*G + j belongs to workgroup j for even k, G-1-j odd)
+  const int nwg = gridDim.x, wg = blockIdx.x;
+  const int total = min(npairs * hkv, a.work_cap);
+  for (int i = t; i < npairs; i += NT) {
+    const int key = pkey[i];
+    const int b = key & (B - 1);
+    const int pos = cnt[b] + cw[(i / S) * B + b] + (key >> 10);
+    const int s = psq[i] & 4095, q = psq[i] >> 12;
+    const int lo = scu[s], len = scu[s + 1] - lo, c = sctx[s];
+    for (int h = 0; h < hkv; ++h) {
+      const int idx = pos * hkv + h;
+      if (idx >= total) break;
+      const int k = idx / nwg, j = idx - k * nwg;
+      if (((k & 1) ? nwg - 1 - j : j) == wg && k < kListCap) {
+        list.m[k] = make_int4(s, q * hkv + h, lo, len);
+        list.c[k] = c;
+      }
+    }
+  }
+  __syncthreads();  // the list is complete and the scratch free for tiles
+  return total;
+}
+
+template <int G, bool INL>
 __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a) {
   __shared__ PrefillShared sm;
-  const int total = a.work[0];
+  __shared__ std::conditional_t<INL, ItemList, int> own;  // this workgroup's items (INL)
+  const ItemList* list = nullptr;
+  int total;
+  if constexpr (INL) {
+    total = plan_inline(a, kPrefillRows / G, reinterpret_cast<int*>(&sm), own);
+    list = &own;
+  } else {
+    total = a.work[0];
+  }
   const int nwg = gridDim.x, wg = blockIdx.x;
   auto rank = [&](int k) { return k * nwg + ((k & 1) ? nwg - 1 - wg : wg); };
   if (rank(0) >= total) return;
@@ -779,11 +976,12 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_kernel(PrefillArgs a)
   ps.tb = 0;
   ps.pre = 0;
   ps.q_ready = false;
-  ItemMeta cur = meta_of(a, load_rec(a, rank(0)));
+  ItemMeta cur = meta_of(a, load_rec<INL>(a, INL ? 0 : rank(0), list));
   for (int k = 0;; ++k) {
     const int nidx = rank(k + 1);  // ranks grow with k: past the end, done
     ItemMeta next;
-    prefill_item<G, false>(a, cur, sm, ps, nidx < total ? nidx : -1, next);
+    prefill_item<G, false, INL>(a, cur, sm, ps, nidx < total ? (INL ? k + 1 : nidx) : -1, list,
+                                next);
     if (nidx >= total) break;
     cur = next;
   }
@@ -802,7 +1000,7 @@ __global__ __launch_bounds__(kPrefillThreads) void cascade_prefix_kernel(Prefill
   ps.pre = 0;
   ps.q_ready = false;
   ItemMeta none;
-  prefill_item<G, true>(a, im, sm, ps, -1, none);
+  prefill_item<G, true>(a, im, sm, ps, -1, nullptr, none);
 }
 
 static int prefill_cus() {
@@ -816,10 +1014,6 @@ static int prefill_cus() {
 
 template <int G>
 static hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a,
-                     prefill_tile_tokens(G));
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
   // resident workgroups per CU (computed once; concurrent first calls compute
   // the same value)
   static std::atomic<int> per_cu_cache{0};
@@ -827,7 +1021,7 @@ static hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t stream) {
   if (per_cu == 0) {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &nb, reinterpret_cast<const void*>(&prefill_kernel<G>), kPrefillThreads, 0) !=
+            &nb, reinterpret_cast<const void*>(&prefill_kernel<G, true>), kPrefillThreads, 0) !=
             hipSuccess ||
         nb <= 0)
       nb = 1;
@@ -840,7 +1034,27 @@ static hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t stream) {
   const char* eg = getenv("PA_PREFILL_GRID");
   if (eg && *eg && atoi(eg) >= 1) want = atoi(eg);
   const int gx = (int)std::max<int64_t>(1, std::min<int64_t>(a.work_cap, want));
-  hipLaunchKernelGGL((prefill_kernel<G>), dim3(gx), dim3(kPrefillThreads), 0, stream, a);
+  // the work list: built inside every workgroup where its bounds allow
+  // (sequences, (sequence, query tile) pairs -- each sequence of two or more
+  // rows has at most rows / tile + 1 of them, and at most rows / 2 -- and
+  // items per workgroup), else by the one-workgroup plan kernel
+  // (PA_PREFILL_INLINE_PLAN=0 forces the plan kernel)
+  const int tile = prefill_tile_tokens(G);
+  const int64_t multi = std::min<int64_t>(a.num_seqs, a.total_q_tokens / 2);
+  const int64_t pairs_bound = std::min<int64_t>((int64_t)a.total_q_tokens / tile + multi + 1,
+                                                (int64_t)a.total_q_tokens / 2 + 1);
+  const char* ei = getenv("PA_PREFILL_INLINE_PLAN");
+  const bool inline_plan = (!ei || atoi(ei) != 0) && a.num_seqs <= kInlineMaxSeqs &&
+                           pairs_bound <= kInlineMaxPairs && ceil_div(a.work_cap, gx) <= kListCap;
+  if (!inline_plan) {
+    hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a, tile);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (inline_plan)
+    hipLaunchKernelGGL((prefill_kernel<G, true>), dim3(gx), dim3(kPrefillThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<G, false>), dim3(gx), dim3(kPrefillThreads), 0, stream, a);
   return hipGetLastError();
 }
 

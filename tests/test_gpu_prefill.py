@@ -205,9 +205,12 @@ def test_prefill_many_items_per_workgroup(gpu, monkeypatch, grid, hq, hkv):
     assert torch.equal(got, ref)
 
 
-def test_packed_call_beyond_plan_lds(gpu):
-    """A packed call of more sequences than the prefill plan holds in LDS
-    (2048): mostly decode rows, a few chunks; the plan's loop path."""
+@pytest.mark.parametrize("inline", ["0", "1"])
+def test_packed_call_beyond_plan_lds(gpu, monkeypatch, inline):
+    """A packed call of more sequences than the prefill plan kernel holds in
+    LDS (2048): mostly decode rows, a few chunks; that kernel's loop path
+    (PA_PREFILL_INLINE_PLAN=0), and the list built in every workgroup."""
+    monkeypatch.setenv("PA_PREFILL_INLINE_PLAN", inline)
     rng = np.random.default_rng(24)
     n = 2100
     q_lens = np.ones(n, dtype=np.int64)
@@ -218,6 +221,62 @@ def test_packed_call_beyond_plan_lds(gpu):
     batch = W.varlen_batch("plan_2100", 24, q_lens, ctx, 32, 8, 128, "bf16")
     seqs = sorted(set(chunk_at + [0, 1, 2000] + rng.choice(n, size=20, replace=False).tolist()))
     _check(batch, seqs=seqs)
+
+
+def _plan_case(kind):
+    """Packed calls at the edges of the in-workgroup work list: many (sequence,
+    query tile) pairs (4000 two-row sequences, each wave of the ranking over
+    500 pairs), the largest sequence count it takes (4096) and one more (the
+    plan kernel's), one kv head per item on a one-row-per-head model, and a
+    grid of 3 workgroups holding about 120 items each."""
+    rng = np.random.default_rng(26)
+    if kind == "pairs_4000":
+        n = 4000
+        return W.varlen_batch(kind, 26, np.full(n, 2), rng.integers(0, 300, size=n), 32, 8, 128,
+                              "bf16"), None
+    if kind in ("seqs_4096", "seqs_4097"):
+        n = int(kind.split("_")[1])
+        q_lens = np.ones(n, dtype=np.int64)
+        at = rng.choice(n, size=40, replace=False)
+        q_lens[at] = rng.integers(2, 200, size=40)
+        q_lens[n - 1] = 77  # the last sequence's end row is read too
+        return W.varlen_batch(kind, 27, q_lens, rng.integers(0, 400, size=n), 32, 8, 128,
+                              "bf16"), None
+    if kind == "mha":
+        return W.varlen_batch(kind, 28, [300, 1, 257, 2, 700, 64], [0, 50, 300, 4, 1, 999],
+                              32, 32, 128, "bf16"), None
+    return W.varlen_batch(kind, 29, [100, 70, 2, 129, 33, 64, 1, 250, 400, 31],
+                          [0, 37, 5, 200, 64, 1000, 300, 17, 2, 90], 32, 8, 128, "bf16"), "3"
+
+
+@pytest.mark.parametrize("kind", ["pairs_4000", "seqs_4096", "seqs_4097", "mha", "grid_3"])
+def test_inline_plan_matches_plan_kernel(gpu, monkeypatch, kind):
+    """Every workgroup builds the longest-first work list itself (no plan
+    launch) when the call fits its bounds; PA_PREFILL_INLINE_PLAN=0 makes the
+    one-workgroup plan kernel build it instead.  Each item's arithmetic does
+    not depend on where it runs, so both give the same output bit for bit --
+    every row written (outputs start as NaN) -- and sampled sequences match
+    the oracle."""
+    batch, grid = _plan_case(kind)
+    if grid:
+        monkeypatch.setenv("PA_PREFILL_GRID", grid)
+    rng = np.random.default_rng(30)
+    n = batch.num_seqs
+    multi = [i for i in range(n) if batch.cu_seqlens[i + 1] - batch.cu_seqlens[i] >= 2]
+    seqs = sorted(set([0, n - 1] + rng.choice(multi, size=min(len(multi), 24),
+                                                replace=False).tolist()))
+    db, out = _check(batch, seqs=seqs)
+    outs = []
+    for inline in ("1", "0"):
+        monkeypatch.setenv("PA_PREFILL_INLINE_PLAN", inline)
+        o = torch.full_like(out, float("nan"))
+        db.attend(out=o)
+        torch.cuda.synchronize()
+        say(kind, "PA_PREFILL_INLINE_PLAN", inline, "all finite", bool(torch.isfinite(o).all()))
+        outs.append(o)
+    assert torch.isfinite(outs[0]).all() and torch.isfinite(outs[1]).all()
+    assert torch.equal(outs[0], outs[1])
+    assert torch.equal(outs[0], out)
 
 
 def test_packed_call_more_rows_than_grid_y(gpu):

@@ -806,6 +806,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const ItemMet
 constexpr int kInlineMaxSeqs = 4096;   // a pair's sequence takes 12 bits of its word
 constexpr int kInlineMaxPairs = 7168;
 
+// Exclusive scan over the workgroup of one value per thread: the thread's
+// offset, and the sum in `total` (wt: one word per wave of scratch).
 __device__ __forceinline__ int inline_scan(int v, int& total, int* wt) {
   constexpr int NW = kPrefillThreads / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;

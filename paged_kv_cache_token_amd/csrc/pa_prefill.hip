@@ -20,7 +20,8 @@
 //     [block][16-byte chunk][key], keys swizzled by chunk; V is read back with
 //     the transposing LDS read).  One barrier per tile: tile t is computed
 //     while tile t+1 waits in LDS and the loads of tile t+2 are in flight;
-//   * the work list is ordered longest first (key tiles per item); one
+//   * the work list is ordered longest first (key tiles per item), built by
+//     every workgroup in LDS (or, for very large calls, by a plan kernel); one
 //     workgroup per CU walks its share in snake order, and while an item runs
 //     its last steps the next item's record, first two key tiles and query
 //     rows are already being loaded, so items follow each other without a
@@ -90,9 +91,10 @@ size_t prefill_work_bytes(int num_seqs, int total_q_tokens, int num_kv_heads, in
 // One workgroup lists the (sequence, query tile, kv head) items of every
 // sequence with two or more query rows, ordered by the number of 64-key tiles
 // they stream, most first (a counting sort in LDS), so the persistent
-// workgroups start the longest items first, on every CU at once.  The order
-// among equal counts is arbitrary: items are independent and each writes only
-// its own rows.  The work is spread over (sequence, query tile) pairs, so a
+// workgroups start the longest items first, on every CU at once.  It serves
+// the calls too large for the list each workgroup builds itself (below).  The
+// order among equal counts is arbitrary: items are independent and each
+// writes only its own rows.  The work is spread over (sequence, query tile) pairs, so a
 // few long chunks do not leave one thread per sequence walking its tiles.
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanMaxSeqs = 2048;  // sequences held in LDS (two per thread)

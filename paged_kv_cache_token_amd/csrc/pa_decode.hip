@@ -1403,6 +1403,15 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t stream) {
   if (a.mfma && a.max_parts - a.prefix_parts > 1 &&
       a.part_tokens <= kBlockSize * kMaxEntriesPerWave && env_int("PA_DECODE_WAVES", 0) == 0)
     a.waves = 1;
+  // Contexts of at most 512 tokens in one partition each, from 2048 (sequence,
+  // kv head) pairs, on the matrix-core code: two waves per item (each wave
+  // still streams several blocks, and the cross-wave merge halves).  Measured
+  // against four in six alternating runs: the LLaMA-2-shaped step 48.86-48.98
+  // us against 49.18-49.27.  Longer contexts keep four (the mixed step's
+  // decode rows of up to 2048 tokens: 0.671 ms with two against 0.659).
+  if (a.mfma && a.max_parts - a.prefix_parts <= 1 && a.waves == 4 && a.max_context_len <= 512 &&
+      (int64_t)a.num_seqs * a.num_kv_heads >= 2048 && env_int("PA_DECODE_WAVES", 0) == 0)
+    a.waves = 2;
   a.inline_plan = decode_inline_plan(a.num_seqs, a.waves) ? 1 : 0;
   // K/V register buffers per wave of the vector item code (bf16 at head_dim
   // 128 with PA_DECODE_MFMA=0), unless set: two on the single-partition
